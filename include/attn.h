@@ -1,0 +1,150 @@
+/*
+ * attn.h -- libattn: exact softmax attention forward on AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * Two operators share one definition: for every sequence and head,
+ *
+ *     out = softmax(scale * Q K^T) V,
+ *
+ * accumulated in fp32 and written in the input's 16-bit type (bf16 or fp16).
+ * The definition and both data layouts are those of the atrex-bench operator
+ * pages "attention_forward" (#001) and "paged_attention_decode" (#024),
+ * sections "Reference Implementation" and "Input Generation".
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is device memory owned by the caller.  The library
+ *    never allocates, frees or synchronises; it writes only `out` and, for
+ *    decode, the caller's `workspace`.
+ *  - Calls enqueue their kernels on `stream` (a hipStream_t; NULL is the null
+ *    stream) and return at once.  They never read device memory on the host.
+ *  - 16-bit tensors are contiguous, row-major, and 16-byte aligned; int32
+ *    index arrays are contiguous and 4-byte aligned.
+ *  - Calls return an attn_status and never print, throw or abort.  Argument
+ *    errors are detected on the host before anything is enqueued; a launch
+ *    failure reported by the HIP runtime maps to ATTN_ERR_HIP.
+ *  - Device-side contents that contradict the sizes passed (cu_seqlens that
+ *    decrease or point past total_q / total_k, block-table entries outside
+ *    [0, num_blocks), seq_lens above max_blocks_per_seq * block_size) are a
+ *    caller error with unspecified output values; the kernels clamp such
+ *    indices so that they never read or write outside the buffers described
+ *    by the size arguments.
+ *  - The library keeps no mutable global state; calls on different streams
+ *    may run concurrently as long as their `out`/`workspace` buffers differ.
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, Hq % Hkv != 0, bad scale */
+    ATTN_ERR_UNSUPPORTED = 2, /* well-formed request outside the built kernels (head_dim, block_size) */
+    ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+    ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_DTYPE_BF16 = 0,
+    ATTN_DTYPE_FP16 = 1
+} attn_dtype;
+
+/*
+ * attn_varlen_fwd -- non-causal variable-length prefill attention.
+ *
+ * Defined by "attention_forward" (#001), Reference Implementation: for each
+ * sequence i, query rows [cu_seqlens_q[i], cu_seqlens_q[i+1]) attend to key
+ * rows [cu_seqlens_k[i], cu_seqlens_k[i+1]) of the same head, with no mask.
+ *
+ *  q              [total_q, num_heads, head_dim], dtype
+ *  k, v           [total_k, num_heads, head_dim], dtype
+ *  cu_seqlens_q   [num_seqs + 1] int32, non-decreasing, cu_seqlens_q[0] >= 0,
+ *                 cu_seqlens_q[num_seqs] <= total_q
+ *  cu_seqlens_k   [num_seqs + 1] int32, the same rules against total_k
+ *  max_seqlen_q   an upper bound on cu_seqlens_q[i+1] - cu_seqlens_q[i]; it
+ *                 sizes the grid, so query rows past it are not computed
+ *  head_dim       72 or 128 (others return ATTN_ERR_UNSUPPORTED)
+ *  scale          finite; the pages use head_dim^-1/2
+ *  out            [total_q, num_heads, head_dim], dtype.  Only rows inside a
+ *                 query segment are written; a sequence with query rows but
+ *                 no key rows gets all-zero rows.  Other rows are untouched.
+ *
+ * num_seqs == 0, max_seqlen_q == 0 or total_q == 0 is a valid no-op.
+ */
+int attn_varlen_fwd(const void *q, const void *k, const void *v,
+                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                    int32_t num_seqs, int32_t max_seqlen_q,
+                    int64_t total_q, int64_t total_k,
+                    int32_t num_heads, int32_t head_dim, float scale,
+                    int32_t dtype, void *out, void *stream);
+
+/*
+ * attn_paged_decode -- single-query attention over a paged KV cache with
+ * grouped-query heads.
+ *
+ * Defined by "paged_attention_decode" (#024), Reference Implementation and
+ * Input Generation.  Token t of sequence s lives in physical block
+ * block_tables[s][t / block_size] at slot t % block_size; query head hq
+ * reads KV head hq / (num_query_heads / num_kv_heads).
+ *
+ *  query          [num_seqs, num_query_heads, head_size], dtype
+ *  k_cache        [num_blocks, num_kv_heads, head_size / 8, block_size, 8]
+ *                 (x = 16 bytes / element size = 8)
+ *  v_cache        [num_blocks, num_kv_heads, head_size, block_size]
+ *  block_tables   [num_seqs, max_blocks_per_seq] int32; only the first
+ *                 ceil(seq_lens[s] / block_size) entries of a row are read
+ *  seq_lens       [num_seqs] int32; seq_lens[s] <= 0 gives an all-zero row
+ *  head_size      128 (others return ATTN_ERR_UNSUPPORTED)
+ *  block_size     16 (others return ATTN_ERR_UNSUPPORTED)
+ *  num_query_heads % num_kv_heads must be 0; the group size
+ *                 num_query_heads / num_kv_heads must be at most 16
+ *  partition_size tokens per split of the context (split-K); 0 picks the
+ *                 library default.  A positive value must be a multiple of
+ *                 block_size.  With more than one partition the kernel writes
+ *                 per-partition (max, sum, partial output) into `workspace`
+ *                 and a second kernel merges them by log-sum-exp.
+ *  workspace      device memory of attn_paged_decode_workspace_size(...)
+ *                 bytes, 256-byte aligned; may be NULL when that size is 0
+ *  out            [num_seqs, num_query_heads, head_size], dtype; every row is
+ *                 written
+ *
+ * num_seqs == 0 is a valid no-op.
+ */
+int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens,
+                      int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                      int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                      int64_t num_blocks, float scale, int32_t dtype,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *out, void *stream);
+
+/*
+ * Number of context partitions attn_paged_decode will use for these sizes
+ * (1 means no split and no workspace).  Returns a negative attn_status
+ * value on invalid sizes.
+ */
+int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,
+                                         int32_t partition_size);
+
+/*
+ * Workspace bytes attn_paged_decode needs for these sizes (0 when one
+ * partition suffices).  Returns 0 on invalid sizes as well; the decode call
+ * itself reports those.
+ */
+size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads,
+                                        int32_t head_size, int32_t max_blocks_per_seq,
+                                        int32_t block_size, int32_t partition_size);
+
+/* A static, human-readable name for a status code. */
+const char *attn_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

@@ -1,0 +1,197 @@
+"""ctypes binding of libattn (``include/attn.h``): argument marshalling only.
+
+Each function here has the name of the C entry point it calls.  It derives the
+scalar sizes from tensor shapes the way the operator pages do
+(atrex-bench "attention_forward" #001 and "paged_attention_decode" #024,
+Reference Implementation: ``num_seqs, num_query_heads, head_size =
+query.shape``, ``num_kv_heads = v_cache.shape[1]``, ``block_size =
+v_cache.shape[3]``), allocates outputs and the decode workspace with torch,
+passes raw device pointers and torch's current HIP stream, and raises on a
+non-OK status.  Every step of the computation runs in the HIP library; if the
+library is missing the call fails loudly -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn.so"
+_lib = None
+
+_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
+_STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+           3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a status other than ATTN_OK."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def library_path():
+    """Where the built HIP library is expected (inside this package)."""
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libattn is not built ({path} is missing); run "
+                           "`python -c 'import __graft_entry__ as g; g.build()'` first")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.attn_varlen_fwd.argtypes = [P, P, P, P, P, i32, i32, i64, i64, i32, i32, f32, i32, P, P]
+    lib.attn_varlen_fwd.restype = ctypes.c_int
+    lib.attn_paged_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32, i32,
+                                      i32, P, sz, P, P]
+    lib.attn_paged_decode.restype = ctypes.c_int
+    lib.attn_paged_decode_num_partitions.argtypes = [i32, i32, i32]
+    lib.attn_paged_decode_num_partitions.restype = i32
+    lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.attn_paged_decode_workspace_size.restype = sz
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, has {t.dim()}")
+
+
+def attn_status_string(status):
+    """The library's name for a status code."""
+    return _load().attn_status_string(int(status)).decode()
+
+
+def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scale=None,
+                    out=None):
+    """Non-causal varlen prefill attention (calls ``attn_varlen_fwd``).
+
+    q [total_q, H, D], k/v [total_k, H, D] in bf16 or fp16; cu_seqlens_* int32
+    [num_seqs + 1] on the GPU.  ``max_seqlen_q`` defaults to the longest
+    query segment (read back from the GPU: a synchronisation).  ``scale``
+    defaults to D**-0.5.  Rows outside every query segment of a
+    caller-provided ``out`` are left untouched.
+    """
+    fp16 = (torch.bfloat16, torch.float16)
+    _need(q, "q", fp16, 3)
+    _need(k, "k", q.dtype, 3)
+    _need(v, "v", q.dtype, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    total_q, H, D = q.shape
+    if k.shape[1:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, H, D] with q's H and D")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries each")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if num_seqs else 0
+    scale = float(D) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    rc = _load().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q), total_q,
+                                 k.shape[0], H, D, scale, _DTYPE[q.dtype], _ptr(out),
+                                 _stream(q.device))
+    if rc != 0:
+        raise AttnError("attn_varlen_fwd", rc)
+    return out
+
+
+def attn_paged_decode_num_partitions(max_blocks_per_seq, block_size, partition_size=0):
+    """Context partitions the decode call will use (calls the C function)."""
+    n = _load().attn_paged_decode_num_partitions(int(max_blocks_per_seq), int(block_size),
+                                                 int(partition_size))
+    if n < 0:
+        raise AttnError("attn_paged_decode_num_partitions", -n)
+    return n
+
+
+def attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, max_blocks_per_seq,
+                                     block_size, partition_size=0):
+    """Workspace bytes for a decode call (calls the C function)."""
+    return _load().attn_paged_decode_workspace_size(int(num_seqs), int(num_query_heads),
+                                                    int(head_size), int(max_blocks_per_seq),
+                                                    int(block_size), int(partition_size))
+
+
+def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=None, out=None,
+                      partition_size=0, workspace=None):
+    """Paged single-query decode with grouped-query heads (calls ``attn_paged_decode``).
+
+    query [num_seqs, Hq, D]; k_cache [num_blocks, Hkv, D/8, block_size, 8];
+    v_cache [num_blocks, Hkv, D, block_size]; block_tables int32
+    [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs].  ``scale``
+    defaults to D**-0.5.  ``partition_size`` (tokens, 0 = library default)
+    sets the split-K granularity; the workspace it needs is allocated here
+    unless one is passed.
+    """
+    fp16 = (torch.bfloat16, torch.float16)
+    _need(query, "query", fp16, 3)
+    _need(k_cache, "k_cache", query.dtype, 5)
+    _need(v_cache, "v_cache", query.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    num_seqs, num_query_heads, head_size = query.shape
+    num_kv_heads = v_cache.shape[1]
+    block_size = v_cache.shape[3]
+    num_blocks = v_cache.shape[0]
+    x = 16 // query.element_size()
+    if tuple(k_cache.shape) != (num_blocks, num_kv_heads, head_size // x, block_size, x):
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_size/8, block_size, 8]")
+    if tuple(v_cache.shape) != (num_blocks, num_kv_heads, head_size, block_size):
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_size, block_size]")
+    if block_tables.shape[0] != num_seqs or seq_lens.numel() != num_seqs:
+        raise ValueError("block_tables and seq_lens need one row/entry per sequence")
+    maxb = block_tables.shape[1]
+    scale = float(head_size) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", query.dtype, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must have query's shape")
+    ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, maxb,
+                                                block_size, partition_size)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = _load().attn_paged_decode(_ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(seq_lens), num_seqs, num_query_heads, num_kv_heads,
+                                   head_size, block_size, maxb, num_blocks, scale,
+                                   _DTYPE[query.dtype], int(partition_size), _ptr(workspace),
+                                   ws_len, _ptr(out), _stream(query.device))
+    if rc != 0:
+        raise AttnError("attn_paged_decode", rc)
+    return out
