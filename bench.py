@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of libattn on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+a varlen prefill call on the 16742-token, 32-head, head_dim-128 sequence and a
+paged-decode call on 256 sequences of 64 tokens (16 query / 16 KV heads,
+head_size 128, block_size 16), sizes from the Shapes tables of the atrex-bench
+pages "attention_forward" (#001, row 9) and "paged_attention_decode" (#024,
+row 0).  Inputs are seeded standard-normal bf16, resident in HBM before the
+timed region.  Each call is bracketed by HIP events on the stream it is
+launched on; the decode inputs rotate over several copies (more bytes than
+the 256 MB Infinity Cache) so every decode call reads HBM, not the cache.
+
+Printed: one JSON line with prefill TFLOP/s (the headline value), decode
+GB/s, both against MI355X roofline peaks, and the CPU oracle's rate on a
+bounded sample (rank 0, one GPU).  Only one GPU is used: --gpus above 1 exits
+with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PREFILL = "prefill_s16742_h32_d128"
+DECODE = "decode_b256_ctx64_h16_kv16_d128"
+KERNEL_SOURCES = ["prefill_kernel.hpp", "decode_kernel.hpp", "device_common.hpp"]
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "softmax_attention_flashattention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel_prefix, src_hash):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_prefix)
+    if not entry or entry.get("source_hash") != src_hash:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def prefill_flops(inp):
+    cq = inp["cu_seqlens_q"].tolist()
+    ck = inp["cu_seqlens_k"].tolist()
+    H, D = inp["q"].shape[1], inp["q"].shape[2]
+    return sum(4.0 * (cq[i + 1] - cq[i]) * (ck[i + 1] - ck[i]) * H * D for i in range(len(cq) - 1))
+
+
+def decode_bytes(inp):
+    """Algorithmic bytes of one decode call: K and V of the tokens in context,
+    the query, the output, the block table and seq_lens."""
+    S, Hq, D = inp["query"].shape
+    Hkv = inp["v_cache"].shape[1]
+    el = inp["query"].element_size()
+    tokens = int(inp["seq_lens"].clamp(min=0).sum())
+    return (2 * tokens * Hkv * D * el + 2 * S * Hq * D * el
+            + inp["block_tables"].numel() * 4 + inp["seq_lens"].numel() * 4)
+
+
+def cpu_baseline(budget_s):
+    """The oracle, as it stands, on a bounded sample of the prefill workload:
+    whole query rows (all keys) of the 16742-token sequence."""
+    import numpy as np
+    import oracle
+    from softmax_attention_flashattention_amd import inputs as gen
+    inp = gen.workload_inputs(PREFILL)
+    S, H, D = inp["q"].shape
+    rng = np.random.default_rng(0)
+    threads = oracle.num_threads()
+
+    def run(n):
+        rows = rng.integers(0, S, n)
+        heads = rng.integers(0, H, n)
+        t0 = time.perf_counter()
+        oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"],
+                               inp["cu_seqlens_k"], rows, heads)
+        return time.perf_counter() - t0
+
+    n = max(threads, 8)
+    t = run(n)
+    n = int(max(n, min(200000, n * (budget_s / max(t, 1e-3)))))
+    t = run(n)
+    flops = 4.0 * n * S * D          # each row: S keys, QK^T and PV
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} (query row, head) pairs of {PREFILL}, each against all {S} keys, "
+                      f"float64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=8,
+                    help="decode input copies cycled through (8 x 138 MB > 256 MB cache)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of CPU work for the oracle baseline (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on a single GPU and no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from softmax_attention_flashattention_amd import attn_paged_decode, attn_varlen_fwd
+    from softmax_attention_flashattention_amd import inputs as gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    p_host = gen.workload_inputs(PREFILL)
+    p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p_host.items()}
+    p_out = torch.empty_like(p["q"])
+    flops = prefill_flops(p_host)
+
+    d_host = gen.workload_inputs(DECODE)
+    d_copies = []
+    for _ in range(max(1, args.rotate)):
+        d_copies.append({k: v.to(dev) for k, v in d_host.items()})
+    d_out = [torch.empty_like(c["query"]) for c in d_copies]
+    dbytes = decode_bytes(d_host)
+
+    def prefill_call():
+        attn_varlen_fwd(p["q"], p["k"], p["v"], p["cu_seqlens_q"], p["cu_seqlens_k"],
+                        max_seqlen_q=p["max_seqlen_q"], out=p_out)
+
+    def decode_call(i):
+        c = d_copies[i % len(d_copies)]
+        attn_paged_decode(c["query"], c["k_cache"], c["v_cache"], c["block_tables"],
+                          c["seq_lens"], out=d_out[i % len(d_copies)])
+
+    for i in range(args.warmup):
+        prefill_call()
+        decode_call(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        a, b, c, d = ev[i]
+        a.record()
+        prefill_call()
+        b.record()
+        c.record()
+        decode_call(args.warmup + i)
+        d.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = sorted(a.elapsed_time(b) for a, b, _, _ in ev)
+    dec_ms = sorted(c.elapsed_time(d) for _, _, c, d in ev)
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    gbs = dbytes / (dec_avg * 1e-3) / 1e9
+
+    src_hash = kernel_source_hash(KERNEL_SOURCES)
+    pre_traffic = profiled_traffic("prefill_fwd_kernel", src_hash)
+    dec_traffic = profiled_traffic("decode_partition_kernel", src_hash)
+
+    result = {
+        "metric": "prefill attn TFLOP/s & % MFMA peak; paged-decode GB/s & % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{PREFILL} + {DECODE}",
+            "prefill": {"seq_lens": [16742], "num_heads": 32, "head_dim": 128,
+                        "scale": "head_dim^-0.5", "causal": False},
+            "decode": {"num_seqs": 256, "ctx_len": 64, "num_query_heads": 16,
+                       "num_kv_heads": 16, "head_size": 128, "block_size": 16,
+                       "input_copies_rotated": len(d_copies)},
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": pre_traffic,
+            "kernel": "prefill_fwd_kernel<128, bf16>",
+            "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
+            "min_launch_ms": round(pre_ms[0], 4),
+        },
+        "decode": {
+            "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {
+                "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
+                "kernel": "decode_partition_kernel<bf16, 1>",
+                "bytes_per_launch": dbytes, "avg_launch_us": round(dec_avg * 1e3, 3),
+                "min_launch_us": round(dec_ms[0] * 1e3, 3),
+            },
+        },
+        "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+        "kernel_source_hash": src_hash,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

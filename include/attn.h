@@ -62,7 +62,8 @@ typedef enum attn_dtype {
  * rows [cu_seqlens_k[i], cu_seqlens_k[i+1]) of the same head, with no mask.
  *
  *  q              [total_q, num_heads, head_dim], dtype
- *  k, v           [total_k, num_heads, head_dim], dtype
+ *  k, v           [total_k, num_heads, head_dim], dtype; may be NULL when
+ *                 total_k == 0
  *  cu_seqlens_q   [num_seqs + 1] int32, non-decreasing, cu_seqlens_q[0] >= 0,
  *                 cu_seqlens_q[num_seqs] <= total_q
  *  cu_seqlens_k   [num_seqs + 1] int32, the same rules against total_k

@@ -1,0 +1,209 @@
+// attn_api.hip -- the C ABI of libattn (declared in include/attn.h):
+// host-side argument validation, kernel selection and launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+#include "decode_kernel.hpp"
+#include "prefill_kernel.hpp"
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 512;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+template <int D, typename T>
+int launch_prefill(const attn::PrefillParams &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(grid), dim3(attn::kPrefillThreads), 0,
+                       stream, p);
+    return launch_status();
+}
+
+template <typename T, int GMAX>
+int launch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn::decode_partition_kernel<T, GMAX>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64), 0, stream, p);
+    int rc = launch_status();
+    if (rc != ATTN_OK || p.num_parts == 1) return rc;
+    hipLaunchKernelGGL((attn::decode_merge_kernel<T>),
+                       dim3(static_cast<unsigned>(static_cast<int64_t>(p.num_seqs) * p.Hq)), dim3(64), 0,
+                       stream, p);
+    return launch_status();
+}
+
+template <typename T>
+int dispatch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
+{
+    if (p.G <= 1) return launch_decode<T, 1>(p, grid, stream);
+    if (p.G <= 2) return launch_decode<T, 2>(p, grid, stream);
+    if (p.G <= 4) return launch_decode<T, 4>(p, grid, stream);
+    if (p.G <= 8) return launch_decode<T, 8>(p, grid, stream);
+    return launch_decode<T, 16>(p, grid, stream);
+}
+
+int partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size, int *part_blocks)
+{
+    if (max_blocks_per_seq < 0 || block_size <= 0 || partition_size < 0) return -ATTN_ERR_INVALID_ARG;
+    if (partition_size % block_size) return -ATTN_ERR_INVALID_ARG;
+    const int pt = partition_size > 0 ? partition_size : kDefaultPartitionTokens;
+    int pb = pt / block_size;
+    if (pb < 1) pb = 1;
+    if (part_blocks) *part_blocks = pb;
+    if (max_blocks_per_seq == 0) return 1;
+    return (max_blocks_per_seq + pb - 1) / pb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int32_t status)
+{
+    switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_ERR_UNKNOWN";
+    }
+}
+
+int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                    const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                    int64_t total_q, int64_t total_k, int32_t num_heads, int32_t head_dim,
+                    float scale, int32_t dtype, void *out, void *stream)
+{
+    if (num_seqs < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || num_heads <= 0 ||
+        head_dim <= 0)
+        return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (head_dim != 72 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+    if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ATTN_ERR_INVALID_ARG;
+    if ((!k || !v) && total_k > 0) return ATTN_ERR_INVALID_ARG;   // k, v may be empty
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return ATTN_ERR_INVALID_ARG;
+
+    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBM - 1) / attn::kPrefillBM;
+    const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
+    const int64_t per_xcd = (work + 7) / 8;
+    if (per_xcd * 8 > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+
+    attn::PrefillParams p;
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.out = static_cast<uint16_t *>(out);
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.num_heads = num_heads;
+    p.num_qtiles = static_cast<int>(qtiles);
+    p.total_work = static_cast<int>(work);
+    p.per_xcd = static_cast<int>(per_xcd);
+    p.scale_log2e = scale * attn::kLog2e;
+    const int grid = static_cast<int>(per_xcd * 8);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (head_dim == 128)
+        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16>(p, grid, s)
+                                        : launch_prefill<128, attn::Fp16>(p, grid, s);
+    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16>(p, grid, s)
+                                    : launch_prefill<72, attn::Fp16>(p, grid, s);
+}
+
+int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,
+                                         int32_t partition_size)
+{
+    return partitions(max_blocks_per_seq, block_size, partition_size, nullptr);
+}
+
+size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads, int32_t head_size,
+                                        int32_t max_blocks_per_seq, int32_t block_size,
+                                        int32_t partition_size)
+{
+    if (num_seqs < 0 || num_query_heads <= 0 || head_size <= 0) return 0;
+    const int np = partitions(max_blocks_per_seq, block_size, partition_size, nullptr);
+    if (np <= 1) return 0;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_query_heads * np;
+    const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+    return ml + rows * static_cast<size_t>(head_size) * sizeof(float);
+}
+
+int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
+                      int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                      int32_t dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *out, void *stream)
+{
+    if (num_seqs < 0 || num_query_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+        block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 || partition_size < 0)
+        return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (num_query_heads % num_kv_heads) return ATTN_ERR_INVALID_ARG;
+    if (head_size % 8) return ATTN_ERR_INVALID_ARG;
+    if (partition_size % block_size) return ATTN_ERR_INVALID_ARG;
+    if (head_size != attn::kDecodeD || block_size != attn::kDecodeBS) return ATTN_ERR_UNSUPPORTED;
+    const int G = num_query_heads / num_kv_heads;
+    if (G > 16) return ATTN_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return ATTN_OK;
+    if (!query || !k_cache || !v_cache || !seq_lens || !out) return ATTN_ERR_INVALID_ARG;
+    if (!block_tables && max_blocks_per_seq > 0) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+        return ATTN_ERR_INVALID_ARG;
+
+    int part_blocks = 1;
+    const int np = partitions(max_blocks_per_seq, block_size, partition_size, &part_blocks);
+    if (np < 1) return ATTN_ERR_INVALID_ARG;
+    const int64_t grid = static_cast<int64_t>(num_seqs) * num_kv_heads * np;
+    if (grid > INT32_MAX || static_cast<int64_t>(num_seqs) * num_query_heads > INT32_MAX)
+        return ATTN_ERR_INVALID_ARG;
+
+    attn::DecodeParams p;
+    p.query = static_cast<const uint16_t *>(query);
+    p.k_cache = static_cast<const uint16_t *>(k_cache);
+    p.v_cache = static_cast<const uint16_t *>(v_cache);
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.out = static_cast<uint16_t *>(out);
+    p.ws_ml = nullptr;
+    p.ws_o = nullptr;
+    if (np > 1) {
+        const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size,
+                                                             max_blocks_per_seq, block_size,
+                                                             partition_size);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return ATTN_ERR_WORKSPACE;
+        const size_t rows = static_cast<size_t>(num_seqs) * num_query_heads * np;
+        const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+        p.ws_ml = static_cast<float *>(workspace);
+        p.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + ml);
+    }
+    p.num_blocks = num_blocks;
+    p.num_seqs = num_seqs;
+    p.Hq = num_query_heads;
+    p.Hkv = num_kv_heads;
+    p.G = G;
+    p.maxb = max_blocks_per_seq;
+    p.part_blocks = part_blocks;
+    p.num_parts = np;
+    p.scale_log2e = scale * attn::kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, grid, s)
+                                    : dispatch_decode<attn::Fp16>(p, grid, s);
+}
+
+}  // extern "C"

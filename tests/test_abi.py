@@ -1,0 +1,131 @@
+"""The C ABI of libattn without a GPU: the library loads, exports every
+function include/attn.h declares, and rejects bad arguments on the host
+before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+LIB = os.path.join(ROOT, "softmax_attention_flashattention_amd", "libattn.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 4096          # an aligned, never-dereferenced stand-in for a device pointer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libattn.so is not built")
+    from softmax_attention_flashattention_amd import binding
+    return binding._load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"attn_varlen_fwd", "attn_paged_decode", "attn_status_string",
+                          "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.attn_status_string(0) == b"ATTN_OK"
+    assert lib.attn_status_string(1) == b"ATTN_ERR_INVALID_ARG"
+    assert lib.attn_status_string(2) == b"ATTN_ERR_UNSUPPORTED"
+    assert lib.attn_status_string(3) == b"ATTN_ERR_WORKSPACE"
+    assert lib.attn_status_string(4) == b"ATTN_ERR_HIP"
+    assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
+
+
+def varlen(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, max_seqlen_q=16,
+             total_q=16, total_k=16, num_heads=2, head_dim=128, scale=0.1, dtype=0, out=FAKE)
+    a.update(kw)
+    return lib.attn_varlen_fwd(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"],
+                               a["max_seqlen_q"], a["total_q"], a["total_k"], a["num_heads"],
+                               a["head_dim"], a["scale"], a["dtype"], a["out"], None)
+
+
+def test_varlen_argument_errors(lib):
+    assert varlen(lib, head_dim=64) == UNSUPPORTED
+    assert varlen(lib, head_dim=0) == INVALID
+    assert varlen(lib, num_heads=0) == INVALID
+    assert varlen(lib, num_seqs=-1) == INVALID
+    assert varlen(lib, max_seqlen_q=-5) == INVALID
+    assert varlen(lib, total_k=-1) == INVALID
+    assert varlen(lib, dtype=7) == INVALID
+    assert varlen(lib, scale=float("nan")) == INVALID
+    assert varlen(lib, scale=float("inf")) == INVALID
+    assert varlen(lib, q=None) == INVALID
+    assert varlen(lib, out=None) == INVALID
+    assert varlen(lib, cu_k=None) == INVALID
+    assert varlen(lib, k=None) == INVALID              # keys exist (total_k = 16)
+    assert varlen(lib, k=FAKE + 8) == INVALID          # not 16-byte aligned
+    assert varlen(lib, cu_q=FAKE + 2) == INVALID       # not 4-byte aligned
+
+
+def test_varlen_empty_work_is_ok_without_launch(lib):
+    assert varlen(lib, num_seqs=0, q=None, out=None) == OK
+    assert varlen(lib, max_seqlen_q=0, q=None) == OK
+    assert varlen(lib, total_q=0, q=None) == OK
+
+
+def decode(lib, **kw):
+    a = dict(query=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, num_seqs=4, hq=16, hkv=16, d=128,
+             bs=16, maxb=4, nb=32, scale=0.1, dtype=0, part=0, ws=None, ws_bytes=0, out=FAKE)
+    a.update(kw)
+    return lib.attn_paged_decode(a["query"], a["k"], a["v"], a["bt"], a["sl"], a["num_seqs"],
+                                 a["hq"], a["hkv"], a["d"], a["bs"], a["maxb"], a["nb"], a["scale"],
+                                 a["dtype"], a["part"], a["ws"], a["ws_bytes"], a["out"], None)
+
+
+def test_decode_argument_errors(lib):
+    assert decode(lib, hkv=3) == INVALID               # 16 % 3 != 0
+    assert decode(lib, d=64) == UNSUPPORTED
+    assert decode(lib, d=12) == INVALID                # not a multiple of x = 8
+    assert decode(lib, bs=32) == UNSUPPORTED
+    assert decode(lib, hq=34, hkv=2) == UNSUPPORTED    # group of 17
+    assert decode(lib, part=24) == INVALID             # not a multiple of block_size
+    assert decode(lib, part=-16) == INVALID
+    assert decode(lib, num_seqs=-1) == INVALID
+    assert decode(lib, nb=-1) == INVALID
+    assert decode(lib, dtype=2) == INVALID
+    assert decode(lib, scale=float("nan")) == INVALID
+    assert decode(lib, query=None) == INVALID
+    assert decode(lib, bt=None) == INVALID
+    assert decode(lib, v=FAKE + 4) == INVALID
+    assert decode(lib, sl=FAKE + 1) == INVALID
+
+
+def test_decode_workspace_rules(lib):
+    # 64 blocks per sequence at the default 512-token partition: 2 partitions
+    assert lib.attn_paged_decode_num_partitions(64, 16, 0) == 2
+    assert lib.attn_paged_decode_num_partitions(4, 16, 0) == 1
+    assert lib.attn_paged_decode_num_partitions(4, 16, 16) == 4
+    assert lib.attn_paged_decode_num_partitions(4, 16, 24) == -INVALID
+    need = lib.attn_paged_decode_workspace_size(4, 16, 128, 64, 16, 0)
+    rows = 4 * 16 * 2
+    assert need == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert lib.attn_paged_decode_workspace_size(4, 16, 128, 4, 16, 0) == 0
+    assert decode(lib, maxb=64, ws=None, ws_bytes=0) == WORKSPACE
+    assert decode(lib, maxb=64, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    assert decode(lib, maxb=64, ws=FAKE + 16, ws_bytes=need) == WORKSPACE   # not 256-aligned
+
+
+def test_decode_empty_batch_is_ok_without_launch(lib):
+    assert decode(lib, num_seqs=0, query=None) == OK
+
+
+def test_binding_names_match_the_header():
+    import softmax_attention_flashattention_amd as pkg
+    for n in declared_functions():
+        assert hasattr(pkg, n), f"binding lacks {n}"

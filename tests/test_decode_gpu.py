@@ -1,0 +1,118 @@
+"""GPU parity of attn_paged_decode against the CPU oracle.
+
+Operator: atrex-bench "paged_attention_decode" (#024), Reference
+Implementation and Input Generation.  Every case feeds the HIP library and
+the oracle the same seeded inputs and applies the bar of tests/parity.py.
+Index work is checked bit for bit: a cache whose blocks are moved and whose
+table is rewritten to match must give identical output bits, and a
+one-token context must return the gathered value row exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check, f64, to_gpu
+from softmax_attention_flashattention_amd import attn_paged_decode, inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, partition_size=0):
+    d = to_gpu(inp)
+    o = attn_paged_decode(d["query"], d["k_cache"], d["v_cache"], d["block_tables"],
+                          d["seq_lens"], partition_size=partition_size)
+    torch.cuda.synchronize()
+    return o
+
+
+def ref_of(inp, v_abs=False):
+    v = inp["v_cache"].abs() if v_abs else inp["v_cache"]
+    return oracle.paged_decode(inp["query"], inp["k_cache"], v, inp["block_tables"],
+                               inp["seq_lens"])
+
+
+def full_check(inp, what, partition_size=0, bar1=True):
+    print(f"[decode] {what}", flush=True)
+    out = run(inp, partition_size)
+    return check(f64(out), ref_of(inp), what, ref_abs=ref_of(inp, True), bar1=bar1), out
+
+
+def test_workload_b256_ctx64_h16_kv16_d128():
+    full_check(gen.workload_inputs("decode_b256_ctx64_h16_kv16_d128"),
+               "decode_b256_ctx64_h16_kv16_d128")
+
+
+def test_permuted_block_table_is_bitwise_identical():
+    inp = gen.decode_inputs(64, 100, 8, 4, 128, seed=3,
+                            seq_lens=[100, 1, 16, 17, 0, 64, 33, 99] * 8)
+    per = gen.permute_blocks(inp, seed=11)
+    a = run(inp).cpu()
+    b = run(per).cpu()
+    assert torch.equal(a, b)
+    check(f64(a), ref_of(inp), "identity table", ref_abs=ref_of(inp, True))
+
+
+def test_ragged_and_empty_contexts():
+    lens = [1, 2, 15, 16, 17, 31, 33, 47, 48, 49, 63, 64, 0, -3, 5, 60]
+    inp = gen.decode_inputs(16, 64, 4, 4, 128, seed=5, seq_lens=lens)
+    _, out = full_check(inp, "ragged contexts")
+    o = out.cpu()
+    assert torch.count_nonzero(o[12]).item() == 0 and torch.count_nonzero(o[13]).item() == 0
+
+
+def test_one_token_context_returns_value_row_exactly():
+    inp = gen.decode_inputs(8, 1, 4, 2, 128, seed=7)
+    per = gen.permute_blocks(inp, seed=8)
+    out = run(per).cpu()
+    for s in range(8):
+        b = int(per["block_tables"][s, 0])
+        for hq in range(4):
+            v = per["v_cache"][b, hq // 2, :, 0]      # token 0 of the block: [D]
+            assert torch.equal(out[s, hq], v), (s, hq)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 16), (16, 8), (32, 8), (40, 8), (12, 4), (64, 8),
+                                    (32, 2), (16, 1)])
+def test_grouped_query_heads(dtype, Hq, Hkv):
+    inp = gen.decode_inputs(6, 128, Hq, Hkv, 128, seed=Hq * 100 + Hkv, dtype=dtype,
+                            seq_lens=[128, 77, 1, 16, 100, 0])
+    full_check(inp, f"GQA {dtype} Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("partition_size", [16, 48, 112, 256])
+@pytest.mark.parametrize("G", [1, 4])
+def test_split_context_merge(partition_size, G):
+    lens = [1000, 333, 17, 0, 512, 1]
+    inp = gen.decode_inputs(6, 1000, 4 * G, 4, 128, seed=51 + G, seq_lens=lens)
+    (_, _), split = full_check(inp, f"split P={partition_size} G={G}", partition_size)
+    whole = run(inp, partition_size=16 * 64)            # one partition
+    assert torch.count_nonzero(split[3]).item() == 0
+    check(f64(split), f64(whole).astype(np.float64), "split vs whole")
+
+
+@pytest.mark.parametrize("ctx,num_seqs", [(4096, 4), (32768, 2)])
+def test_long_contexts(ctx, num_seqs):
+    inp = gen.decode_inputs(num_seqs, ctx, 8, 2, 128, seed=ctx)
+    full_check(inp, f"long ctx {ctx}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_page_table_rows(dtype):
+    # the remaining rows of the decode Shapes table that fit head_size 128
+    for (S, L, Hq, Hkv) in [(128, 64, 3, 3), (4, 128, 32, 4), (4, 128, 32, 8), (1, 128, 4, 1),
+                            (4, 128, 40, 8), (4, 128, 64, 8)]:
+        full_check(gen.decode_inputs(S, L, Hq, Hkv, 128, seed=S + L + Hq, dtype=dtype),
+                   f"table row {S}x{L} Hq={Hq} Hkv={Hkv} {dtype}")
+
+
+def test_scaled_values_tighten_the_floor():
+    inp = gen.decode_inputs(32, 300, 8, 2, 128, seed=61)
+    inp["v_cache"] = (inp["v_cache"].float() * 64.0).to(torch.bfloat16)
+    full_check(inp, "V*64", bar1=False)
+
+
+def test_runs_are_bitwise_deterministic():
+    inp = gen.decode_inputs(16, 700, 8, 2, 128, seed=71)
+    assert torch.equal(run(inp, 64).cpu(), run(inp, 64).cpu())

@@ -1,0 +1,144 @@
+"""GPU parity of attn_varlen_fwd against the CPU oracle.
+
+Operator: atrex-bench "attention_forward" (#001), Reference Implementation.
+Every case feeds the HIP library and the oracle the same seeded inputs and
+applies the bar of tests/parity.py elementwise.  Full-size workloads are
+checked on sampled (row, head) pairs the oracle evaluates one by one,
+including the first and last rows (the partial last query tile).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check, f64, to_gpu
+from softmax_attention_flashattention_amd import attn_varlen_fwd, inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -12352.0      # exactly representable in bf16 and fp16
+
+
+def run(inp, out=None):
+    d = to_gpu(inp)
+    o = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                        max_seqlen_q=inp["max_seqlen_q"], out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def refs(inp):
+    """Oracle output and the oracle on |v| (the scale of bar 2)."""
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    ref = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), *args)
+    return ref, ref_abs
+
+
+def full_check(inp, what, bar1=True):
+    print(f"[prefill] {what}", flush=True)
+    out = run(inp)
+    ref, ref_abs = refs(inp)
+    m = ~np.isnan(ref)
+    return check(f64(out)[m], ref[m], what, ref_abs=ref_abs[m], bar1=bar1)
+
+
+@pytest.mark.parametrize("D", [72, 128])
+@pytest.mark.parametrize("S", [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 276])
+def test_single_sequence_lengths(D, S):
+    full_check(gen.prefill_inputs([S], 2, D, seed=100 + S), f"S={S} D={D}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("D", [72, 128])
+def test_varlen_batch_with_empty_and_unequal_segments(dtype, D):
+    # an empty query segment, S_q != S_k, a sequence with no keys, ragged tiles
+    inp = gen.prefill_inputs([5, 0, 300, 64, 129, 1], 3, D, seed=7, dtype=dtype,
+                             seq_lens_k=[7, 3, 250, 0, 129, 200])
+    full_check(inp, f"varlen {dtype} D={D}")
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_rows_outside_segments_are_untouched(D):
+    inp = gen.prefill_inputs([40, 70], 2, D, seed=9)
+    # 30 extra rows after the last segment belong to no sequence
+    pad = torch.zeros(30, 2, D, dtype=torch.bfloat16)
+    inp["q"] = torch.cat([inp["q"], pad])
+    d = to_gpu(inp)
+    out = torch.full_like(d["q"], SENTINEL)
+    attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=70, out=out)
+    torch.cuda.synchronize()
+    o = f64(out)
+    assert np.all(o[110:] == SENTINEL)
+    ref, ref_abs = refs(inp)
+    check(o[:110], ref[:110], f"sentinel D={D}", ref_abs=ref_abs[:110])
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_scaled_values_tighten_the_floor(D):
+    # out is linear in V and a power-of-two scale is exact in bf16; with V
+    # scaled up the output errors are judged by the scale-free bar 2 only.
+    inp = gen.prefill_inputs([1000], 2, D, seed=21, v_scale=64.0)
+    full_check(inp, f"V*64 D={D}", bar1=False)
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_single_key_returns_value_rows_exactly(D):
+    # one key per sequence: softmax weight 1, so out == v bit for bit
+    inp = gen.prefill_inputs([50, 3], 4, D, seed=31, seq_lens_k=[1, 1])
+    out = run(inp)
+    v = inp["v"]
+    assert torch.equal(out[:50].cpu(), v[0:1].expand(50, 4, D))
+    assert torch.equal(out[50:].cpu(), v[1:2].expand(3, 4, D))
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_identical_value_rows_return_that_row(D):
+    inp = gen.prefill_inputs([300], 2, D, seed=33)
+    inp["v"] = inp["v"][7:8].expand(300, 2, D).contiguous()
+    out = f64(run(inp))
+    row = f64(inp["v"][7])
+    # within one bf16 ulp of the row
+    assert np.all(np.abs(out - row[None]) <= 2.0 ** -7 * np.abs(row[None]) + 1e-30)
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_no_keys_gives_zero_rows(D):
+    inp = gen.prefill_inputs([17], 2, D, seed=35, seq_lens_k=[0])
+    out = run(inp)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_runs_are_bitwise_deterministic():
+    inp = gen.prefill_inputs([777], 4, 128, seed=41)
+    a = run(inp).cpu()
+    b = run(inp).cpu()
+    assert torch.equal(a, b)
+
+
+def sampled_check(name, n_rows=48, seed=7):
+    inp = gen.workload_inputs(name)
+    S = inp["q"].shape[0]
+    H = inp["q"].shape[1]
+    print(f"[prefill] workload {name}", flush=True)
+    out = run(inp)
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, S - 1, S - 2, (S // 128) * 128], rng.integers(0, S, n_rows)])
+    rows = np.clip(rows, 0, S - 1)
+    heads = rng.integers(0, H, rows.size)
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
+    return check(got, ref, name, ref_abs=ref_abs)
+
+
+def test_workload_s276_h4_d72_full():
+    full_check(gen.workload_inputs("prefill_s276_h4_d72"), "prefill_s276_h4_d72")
+
+
+@pytest.mark.parametrize("name", ["prefill_s8136_h16_d72", "prefill_s16742_h32_d128",
+                                  "prefill_s65556_h16_d72"])
+def test_workload_sampled_rows(name):
+    sampled_check(name)
