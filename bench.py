@@ -103,6 +103,26 @@ def cpu_baseline(budget_s):
                       f"float64, {t:.1f} s"}
 
 
+def copy_reference(torch, dev, args):
+    """A plain 1 GiB device-to-device copy (torch's copy kernel): its measured
+    bandwidth, and the reference launch for scaling HBM byte counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "avg_ms": round(ms, 4),
+                      "GB/s (read + write)": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +132,9 @@ def main():
                     help="decode input copies cycled through (8 x 138 MB > 256 MB cache)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU work for the oracle baseline (0 skips it)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="time one part alone (for profiling); 'copy' times a plain 1 GiB "
+                         "device-to-device copy, the reference for HBM counter scaling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -125,6 +148,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
+    if args.only == "copy":
+        return copy_reference(torch, dev, args)
 
     p_host = gen.workload_inputs(PREFILL)
     p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p_host.items()}
@@ -147,9 +172,13 @@ def main():
         attn_paged_decode(c["query"], c["k_cache"], c["v_cache"], c["block_tables"],
                           c["seq_lens"], out=d_out[i % len(d_copies)])
 
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
     for i in range(args.warmup):
-        prefill_call()
-        decode_call(i)
+        if do_prefill:
+            prefill_call()
+        if do_decode:
+            decode_call(i)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -160,10 +189,12 @@ def main():
     for i in range(args.steps):
         a, b, c, d = ev[i]
         a.record()
-        prefill_call()
+        if do_prefill:
+            prefill_call()
         b.record()
         c.record()
-        decode_call(args.warmup + i)
+        if do_decode:
+            decode_call(args.warmup + i)
         d.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -172,8 +203,8 @@ def main():
     dec_ms = sorted(c.elapsed_time(d) for _, _, c, d in ev)
     pre_avg = sum(pre_ms) / len(pre_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
-    tflops = flops / (pre_avg * 1e-3) / 1e12
-    gbs = dbytes / (dec_avg * 1e-3) / 1e9
+    tflops = flops / (pre_avg * 1e-3) / 1e12 if do_prefill else 0.0
+    gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_decode else 0.0
 
     src_hash = kernel_source_hash(KERNEL_SOURCES)
     pre_traffic = profiled_traffic("prefill_fwd_kernel", src_hash)
@@ -222,7 +253,9 @@ def main():
                    "cus": props.multi_processor_count},
         "kernel_source_hash": src_hash,
     }
-    if args.cpu_budget > 0:
+    if args.only is not None:
+        result["only"] = args.only
+    if args.cpu_budget > 0 and args.only is None:
         result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     else:
         result["cpu_baseline"] = None

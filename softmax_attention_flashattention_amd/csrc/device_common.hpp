@@ -33,6 +33,19 @@ struct Bf16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
+    // acc + lo(w) + hi(w): the two packed 16-bit values of w summed in fp32
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+    }
+    // two fp32 -> two bf16 (lo first), round to nearest even, one v_cvt_pk_bf16_f32
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static constexpr uint32_t one_bits = 0x3F80u;
 };
 
 struct Fp16 {
@@ -49,12 +62,33 @@ struct Fp16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    static constexpr uint32_t one_bits = 0x3C00u;
 };
+
+// Buffer resource for raw 16-byte loads of [base, base + num_bytes): loads
+// past num_bytes return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(num_bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 0));
+}
 
 // Packs two fp32 values into one dword of two 16-bit elements (lo first).
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return static_cast<uint32_t>(T::from_f32(lo)) | (static_cast<uint32_t>(T::from_f32(hi)) << 16);
+    return T::pack2(lo, hi);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

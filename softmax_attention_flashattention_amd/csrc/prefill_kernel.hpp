@@ -8,8 +8,11 @@
 // Work decomposition.  One workgroup (4 waves) owns a tile of BM = 128 query
 // rows of one (sequence, head); each wave owns 32 of those rows.  The
 // workgroup streams the sequence's keys and values in tiles of BN = 64 rows
-// through LDS (double-buffered, staged through registers so the next tile's
-// global loads are in flight while the current tile is computed).
+// through double-buffered LDS.  For head_dim 128 the tiles go from global
+// memory straight into LDS (buffer loads with the LDS destination bit), laid
+// out unpadded with an XOR swizzle of the 16-byte chunks of each row so that
+// the MFMA operand reads hit distinct banks; head_dim 72 stages them through
+// registers into padded rows.
 //
 // Both contractions run on 32x32x16 MFMA with fp32 accumulation, computed
 // transposed so that each lane owns one query row:
@@ -33,6 +36,8 @@
 // actually multiplied V (the padding does useful work instead of a VALU sum).
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace attn {
@@ -53,14 +58,16 @@ template <int D> struct PrefillShape;
 template <> struct PrefillShape<128> {
     static constexpr int KSTEPS = 8;    // QK^T contraction steps of 16
     static constexpr int DBLK = 4;      // O^T row blocks of 32
-    static constexpr int KPITCH = 136;  // K tile row pitch, elements (272 B: 16 lanes hit distinct banks)
-    static constexpr int VPITCH = 160;  // V tile row pitch (320 B: 4 rows land 16 banks apart)
+    static constexpr bool DIRECT = true;  // global -> LDS without registers
+    static constexpr int KPITCH = 128;  // unpadded rows; chunks XOR-swizzled
+    static constexpr int VPITCH = 128;
     static constexpr int ONES_COL = -1;
 };
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
     static constexpr int DBLK = 3;      // 72 padded to 96
-    static constexpr int KPITCH = 88;   // 176 B
+    static constexpr bool DIRECT = false;
+    static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
 };
@@ -69,23 +76,39 @@ constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
 constexpr int kPrefillThreads = 256;
 
-template <typename T> struct One16;
-template <> struct One16<Bf16> { static constexpr uint32_t bits = 0x3F80u; };
-template <> struct One16<Fp16> { static constexpr uint32_t bits = 0x3C00u; };
+// Rescaling threshold (log2 units) of the lazy online softmax: the running
+// max is raised, and O, l rescaled, only when some row's new max exceeds it by
+// more than this; otherwise p = exp2(c s - m) may reach 2^8, harmless in fp32
+// and in the 16-bit P operand (the result is shift-invariant).
+constexpr float kRescaleThreshold = 8.0f;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D, typename T>
 __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_fwd_kernel(PrefillParams p)
 {
     using S = PrefillShape<D>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     constexpr int BM = kPrefillBM, BN = kPrefillBN;
     constexpr int KP = S::KPITCH, VP = S::VPITCH;
     constexpr int CH = D / 8;                      // 16-byte chunks per row
     constexpr int NCH = BN * CH;                   // chunks per K (or V) tile
     constexpr int PER = (NCH + kPrefillThreads - 1) / kPrefillThreads;
+    constexpr bool DIRECT = S::DIRECT;
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][BN * VP];
+    // one array per buffer, so that the compiler can tell the buffers apart
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds0[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds1[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds0[BN * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds1[BN * VP];
+    auto kbuf = [&](auto par) -> uint16_t * {
+        if constexpr (decltype(par)::value == 0) return k_lds0; else return k_lds1;
+    };
+    auto vbuf = [&](auto par) -> uint16_t * {
+        if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
+    };
 
     // XCD-aware work id: hardware hands consecutive workgroups to the 8 XCDs
     // in turn, so bid -> (bid % 8) * per_xcd + bid / 8 keeps runs of
@@ -113,21 +136,26 @@ void prefill_fwd_kernel(PrefillParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int64_t rs = static_cast<int64_t>(p.num_heads) * D;   // token row stride
-    const uint16_t *kbase_ptr = p.k + ka * rs + head * D;
-    const uint16_t *vbase_ptr = p.v + ka * rs + head * D;
+    const int64_t rs = static_cast<int64_t>(p.num_heads) * D;   // token row stride, elements
+    const uint32_t row_bytes = static_cast<uint32_t>(rs * 2);
+    const uint16_t *k_head = p.k + ka * rs + head * D;
+    const uint16_t *v_head = p.v + ka * rs + head * D;
+    const float c = p.scale_log2e;
 
     if constexpr (S::ONES_COL >= 0) {
         // constant pad columns of both buffers: K cols 72..79 = 0,
         // V col 72 = 1, V cols 73..95 = 0
         const uint4 z = {0u, 0u, 0u, 0u};
-        const uint4 one = {One16<T>::bits, 0u, 0u, 0u};
-        for (int i = tid; i < 2 * BN; i += kPrefillThreads) {
-            const int buf = i / BN, r = i % BN;
-            st16(&k_lds[buf][r * KP + 72], z);
-            st16(&v_lds[buf][r * VP + 72], one);
-            st16(&v_lds[buf][r * VP + 80], z);
-            st16(&v_lds[buf][r * VP + 88], z);
+        const uint4 one = {T::one_bits, 0u, 0u, 0u};
+        for (int r = tid; r < BN; r += kPrefillThreads) {
+            st16(&k_lds0[r * KP + 72], z);
+            st16(&k_lds1[r * KP + 72], z);
+            st16(&v_lds0[r * VP + 72], one);
+            st16(&v_lds0[r * VP + 80], z);
+            st16(&v_lds0[r * VP + 88], z);
+            st16(&v_lds1[r * VP + 72], one);
+            st16(&v_lds1[r * VP + 80], z);
+            st16(&v_lds1[r * VP + 88], z);
         }
     }
 
@@ -143,76 +171,124 @@ void prefill_fwd_kernel(PrefillParams p)
         qreg[ks] = __builtin_bit_cast(s16x8, v4);
     }
 
+    // ---- tile movement.  Each tile gets its own buffer resource whose extent
+    // ends at the sequence's last key (zero past the last tile), so rows past
+    // the end read as zeros and loads past the last tile fetch nothing.
     const int ntiles = (Sk + BN - 1) / BN;
+    auto tile_bytes = [&](int t) -> uint32_t {
+        const int rows = Sk - t * BN < BN ? Sk - t * BN : BN;
+        return rows > 0 ? static_cast<uint32_t>(rows - 1) * row_bytes + D * 2u : 0u;
+    };
+
+    // Direct path (head_dim 128): instruction j of wave w fills LDS rows
+    // 16 w + 4 j .. +3 (1 KiB, lane i -> bytes 16 i .. 16 i + 15).  Row R keeps
+    // logical chunk c at position c ^ (R % 16) for K and c ^ 4 (R % 4) for V.
+    uint32_t dk_off[4] = {0u, 0u, 0u, 0u};
+    uint32_t dv_off = 0u;
+    // Staged path (head_dim 72): thread chunks through registers.
+    uint32_t voff[PER];
+    int lds_off_k[PER], lds_off_v[PER];
+    if constexpr (DIRECT) {
+        const int rsub = lane >> 4, pos = lane & 15;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int R = 16 * wave + 4 * j + rsub;
+            dk_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (R & 15));
+        }
+        dv_off = static_cast<uint32_t>(16 * wave + rsub) * row_bytes +
+                 16u * static_cast<uint32_t>(pos ^ (4 * (rsub & 3)));
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int cidx = tid + i * kPrefillThreads;
+            const int r = cidx / CH, col = (cidx % CH) * 8;
+            voff[i] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(col) * 2u;
+            lds_off_k[i] = r * KP + col;
+            lds_off_v[i] = r * VP + col;
+        }
+    }
+    // tail loads of head_dim 72 cover only part of the threads (whole waves)
+    auto active = [&](int i) { return NCH % kPrefillThreads == 0 || tid + i * kPrefillThreads < NCH; };
     uint4 kst[PER], vst[PER];
 
-    auto load_tile = [&](int t) {
+    auto load_k = [&](int t, auto par) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(k_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
+        if constexpr (DIRECT) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + i * kPrefillThreads;
-            uint4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
-            if (c < NCH) {
-                const int r = c / CH, col = (c % CH) * 8;
-                const int key = t * BN + r;
-                if (key < Sk) {
-                    kz = ld16(kbase_ptr + key * rs + col);
-                    vz = ld16(vbase_ptr + key * rs + col);
-                }
-            }
-            kst[i] = kz;
-            vst[i] = vz;
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (lds_void *)(kbuf(par) + (16 * wave + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (active(i)) kst[i] = buf_ld16(r, voff[i]);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto load_v = [&](int t, auto par) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(v_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
+        if constexpr (DIRECT) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + i * kPrefillThreads;
-            if (c < NCH) {
-                const int r = c / CH, col = (c % CH) * 8;
-                st16(&k_lds[buf][r * KP + col], kst[i]);
-                st16(&v_lds[buf][r * VP + col], vst[i]);
-            }
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    r, (lds_void *)(vbuf(par) + (16 * wave + 4 * j) * VP), 16, dv_off,
+                    static_cast<int>(4 * j * row_bytes), 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (active(i)) vst[i] = buf_ld16(r, voff[i]);
         }
     };
-
-    float m_run = -INFINITY;   // running max of c*s for this lane's query
-    float l_run = 0.f;         // this lane's partial row sum (its 16 keys of each 32)
-    f32x16 oacc[S::DBLK];
+    auto store_k = [&](auto par) {
+        if constexpr (!DIRECT) {
 #pragma unroll
-    for (int db = 0; db < S::DBLK; ++db)
+            for (int i = 0; i < PER; ++i)
+                if (active(i)) st16(kbuf(par) + lds_off_k[i], kst[i]);
+        }
+    };
+    auto store_v = [&](auto par) {
+        if constexpr (!DIRECT) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+            for (int i = 0; i < PER; ++i)
+                if (active(i)) st16(vbuf(par) + lds_off_v[i], vst[i]);
+        }
+    };
+    // all tile data of this iteration in LDS and visible to every wave
+    auto tiles_ready = [&]() {
+        if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
+    };
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    // transposed-read addressing of the V tile (see the header comment)
+    // ---- operand addressing (element offsets inside a tile buffer)
+    // K rows for S^T: row 32 kb2 + l32, chunk 2 ks + hi
+    int k_rd[S::KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < S::KSTEPS; ++ks)
+        k_rd[ks] = DIRECT ? l32 * KP + 8 * ((2 * ks + hi) ^ (l32 & 15)) : l32 * KP + 16 * ks + 8 * hi;
+    // V^T by transposed reads: row 16 kc + tr_row (+8), column 32 db + tr_col
     const int g16 = lane >> 4;
     const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
     const int tr_col = 16 * (g16 & 1) + 4 * (lane & 3);
+    int v_rd[S::DBLK];
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
+        v_rd[db] = DIRECT ? tr_row * VP + 8 * ((4 * db + (tr_col >> 3)) ^ (4 * (tr_row & 3))) + (tr_col & 7)
+                          : tr_row * VP + 32 * db + tr_col;
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
-
-        // ---- S^T = K Q^T for two 32-key blocks
-        f32x16 sacc[2];
+    // S^T = K Q^T for the two 32-key blocks of a tile
+    auto compute_s = [&](auto par, f32x16 (&sacc)[2]) {
+        const f32x16 zero = {};
+        const uint16_t *kt = kbuf(par);
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const uint16_t *kr = kt + 32 * kb2 * KP;
+            sacc[kb2] = T::mfma32(*reinterpret_cast<const s16x8 *>(kr + k_rd[0]), qreg[0], zero);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.f;
-            const uint16_t *krow = &k_lds[buf][(32 * kb2 + l32) * KP + 8 * hi];
-#pragma unroll
-            for (int ks = 0; ks < S::KSTEPS; ++ks) {
-                const s16x8 a = *reinterpret_cast<const s16x8 *>(krow + 16 * ks);
-                sacc[kb2] = T::mfma32(a, qreg[ks], sacc[kb2]);
-            }
+            for (int ks = 1; ks < S::KSTEPS; ++ks)
+                sacc[kb2] = T::mfma32(*reinterpret_cast<const s16x8 *>(kr + k_rd[ks]), qreg[ks], sacc[kb2]);
         }
-
-        // ---- mask keys past the end of the sequence (last tile only)
+    };
+    // keys past the end of the sequence (only in the last tile) get -inf
+    auto mask_tail = [&](int t, f32x16 (&sacc)[2]) {
         const int kbase = t * BN;
         if (kbase + BN > Sk) {
 #pragma unroll
@@ -223,61 +299,124 @@ void prefill_fwd_kernel(PrefillParams p)
                     if (key >= Sk) sacc[kb2][r] = -INFINITY;
                 }
         }
+    };
 
-        // ---- online softmax
+    float m_run = -INFINITY;   // running max of c*s for this lane's query (log2 domain)
+    float l_run0 = 0.f, l_run1 = 0.f;   // this lane's partial row sums (two chains)
+    f32x16 oacc[S::DBLK];
+#pragma unroll
+    for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+    // Online softmax of one tile, branch-free: P^T (16-bit, B-operand layout)
+    // from S^T.  Sets the factor O must be scaled by (1 for every lane unless
+    // some row's max moved) and returns whether any lane needs it.
+    auto softmax = [&](f32x16 (&sacc)[2], s16x8 (&pk)[4], float &alpha) -> bool {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
         mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float m_new = fmaxf(m_run, mx * p.scale_log2e);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float cand = mx * c;
+        const float m_new = cand > m_run + kRescaleThreshold ? cand : m_run;
+        alpha = fast_exp2(m_run - m_new);
+        const bool any = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
         m_run = m_new;
-
-        s16x8 pk[4];
-        float rowsum = 0.f;
+        l_run0 *= alpha;
+        l_run1 *= alpha;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kc = 0; kc < 4; ++kc) {
+            uint32_t wd[4];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = fast_exp2(__builtin_fmaf(sacc[kb2][r], p.scale_log2e, -m_new));
-                const float p1 = fast_exp2(__builtin_fmaf(sacc[kb2][r + 1], p.scale_log2e, -m_new));
-                if constexpr (S::ONES_COL < 0) rowsum += p0 + p1;
-                const uint32_t pp = pack2<T>(p0, p1);
-                const int kc = 2 * kb2 + (r >> 3);
-                const int e = r & 7;
-                pk[kc][e] = static_cast<short>(pp & 0xffffu);
-                pk[kc][e + 1] = static_cast<short>(pp >> 16);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 8 * (kc & 1) + 2 * e;
+                const float p0 = fast_exp2(__builtin_fmaf(sacc[kc >> 1][r], c, -m_new));
+                const float p1 = fast_exp2(__builtin_fmaf(sacc[kc >> 1][r + 1], c, -m_new));
+                wd[e] = pack2<T>(p0, p1);
+                if constexpr (S::ONES_COL < 0) {
+                    if (e & 1) l_run1 = T::sum2(wd[e], l_run1);
+                    else l_run0 = T::sum2(wd[e], l_run0);
+                }
             }
-        if constexpr (S::ONES_COL < 0) l_run = l_run * alpha + rowsum;
-#pragma unroll
-        for (int db = 0; db < S::DBLK; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            const uint4 w4 = {wd[0], wd[1], wd[2], wd[3]};
+            pk[kc] = __builtin_bit_cast(s16x8, w4);
+        }
+        return any;
+    };
 
-        // ---- O^T += V^T P^T
+    // O^T += V^T P^T
+    auto pv = [&](auto par, const s16x8 (&pk)[4]) {
+        const uint16_t *vt = vbuf(par);
 #pragma unroll
         for (int db = 0; db < S::DBLK; ++db) {
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
-                const uint16_t *base = &v_lds[buf][(16 * kc + tr_row) * VP + 32 * db + tr_col];
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(base));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(base + 8 * VP));
+                const uint16_t *base = vt + 16 * kc * VP + v_rd[db];
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
                 const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
                 oacc[db] = T::mfma32(a, pk[kc], oacc[db]);
             }
         }
+    };
 
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
-        __syncthreads();
+    // Software pipeline: iteration t computes S for tile t+1 (MFMA) while it
+    // runs the softmax of tile t (VALU), then O += V_t P_t.  K runs one tile
+    // ahead of V in the LDS double buffers; tile t+2 of K and t+1 of V are in
+    // flight from global memory during the iteration.  Past the last tile the
+    // buffer resources have zero extent, so those loads fetch nothing and
+    // return zeros; the extra S block of the last iteration is discarded.
+    f32x16 sa[2], sb[2];
+    s16x8 pk[4];
+    if (ntiles > 0) {
+        load_k(0, P0{});
+        load_v(0, P0{});
+        store_k(P0{});
+        store_v(P0{});
+        load_k(1, P1{});
+        store_k(P1{});
+        tiles_ready();
+        compute_s(P0{}, sa);
+        mask_tail(0, sa);
+        __syncthreads();   // K buffer 0 is refilled at the start of iteration 0
+    }
+    // par = t % 2: K(t) and V(t) live in buffer par, K(t+1) in buffer 1 - par
+    auto step = [&](int t, auto par, auto npar, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        load_k(t + 2, par);
+        load_v(t + 1, npar);
+        compute_s(npar, nxt);
+        float alpha;
+        const bool rescale = softmax(cur, pk, alpha);
+        // interleave the S MFMAs of tile t+1 with the softmax VALU of tile t
+#pragma unroll
+        for (int i = 0; i < 2 * S::KSTEPS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
+        }
+        if (rescale) {
+#pragma unroll
+            for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        pv(par, pk);
+        mask_tail(t + 1, nxt);
+        store_k(par);
+        store_v(npar);
+        tiles_ready();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, P0{}, P1{}, sa, sb);
+        if (t + 1 < ntiles) step(t + 1, P1{}, P0{}, sb, sa);
     }
 
     // ---- epilogue: normalise, round to 16 bits, store rows inside the segment
     float l_tot;
     if constexpr (S::ONES_COL < 0) {
+        const float l_run = l_run0 + l_run1;
         l_tot = l_run + xor_shfl(l_run, 32);
     } else {
         // row 72 of O^T = block 2, register 4, lanes 0..31
