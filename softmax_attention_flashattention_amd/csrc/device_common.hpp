@@ -95,6 +95,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// The value of lane l ^ 32, without going through LDS (v_permlane32_swap).
+__device__ __forceinline__ float swap_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 now hold lanes 32..63
+    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
+// max(v, value of lane l ^ 32)
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }

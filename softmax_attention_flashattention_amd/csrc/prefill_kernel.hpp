@@ -279,13 +279,12 @@ void prefill_fwd_kernel(PrefillParams p)
         const f32x16 zero = {};
         const uint16_t *kt = kbuf(par);
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const uint16_t *kr = kt + 32 * kb2 * KP;
-            sacc[kb2] = T::mfma32(*reinterpret_cast<const s16x8 *>(kr + k_rd[0]), qreg[0], zero);
+        for (int ks = 0; ks < S::KSTEPS; ++ks)
 #pragma unroll
-            for (int ks = 1; ks < S::KSTEPS; ++ks)
-                sacc[kb2] = T::mfma32(*reinterpret_cast<const s16x8 *>(kr + k_rd[ks]), qreg[ks], sacc[kb2]);
-        }
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const s16x8 a = *reinterpret_cast<const s16x8 *>(kt + 32 * kb2 * KP + k_rd[ks]);
+                sacc[kb2] = T::mfma32(a, qreg[ks], ks == 0 ? zero : sacc[kb2]);
+            }
     };
     // keys past the end of the sequence (only in the last tile) get -inf
     auto mask_tail = [&](int t, f32x16 (&sacc)[2]) {
@@ -309,55 +308,20 @@ void prefill_fwd_kernel(PrefillParams p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-    // Online softmax of one tile, branch-free: P^T (16-bit, B-operand layout)
-    // from S^T.  Sets the factor O must be scaled by (1 for every lane unless
-    // some row's max moved) and returns whether any lane needs it.
-    auto softmax = [&](f32x16 (&sacc)[2], s16x8 (&pk)[4], float &alpha) -> bool {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-        mx = fmaxf(mx, xor_shfl(mx, 32));
-        const float cand = mx * c;
-        const float m_new = cand > m_run + kRescaleThreshold ? cand : m_run;
-        alpha = fast_exp2(m_run - m_new);
-        const bool any = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
-        m_run = m_new;
-        l_run0 *= alpha;
-        l_run1 *= alpha;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            uint32_t wd[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 8 * (kc & 1) + 2 * e;
-                const float p0 = fast_exp2(__builtin_fmaf(sacc[kc >> 1][r], c, -m_new));
-                const float p1 = fast_exp2(__builtin_fmaf(sacc[kc >> 1][r + 1], c, -m_new));
-                wd[e] = pack2<T>(p0, p1);
-                if constexpr (S::ONES_COL < 0) {
-                    if (e & 1) l_run1 = T::sum2(wd[e], l_run1);
-                    else l_run0 = T::sum2(wd[e], l_run0);
-                }
-            }
-            const uint4 w4 = {wd[0], wd[1], wd[2], wd[3]};
-            pk[kc] = __builtin_bit_cast(s16x8, w4);
-        }
-        return any;
-    };
-
-    // O^T += V^T P^T
-    auto pv = [&](auto par, const s16x8 (&pk)[4]) {
+    // O^T += V^T P^T.  kc outer, db inner: consecutive MFMAs are independent.
+    auto pv = [&](auto par, const uint32_t (&pw)[16]) {
         const uint16_t *vt = vbuf(par);
 #pragma unroll
-        for (int db = 0; db < S::DBLK; ++db) {
+        for (int kc = 0; kc < 4; ++kc) {
+            const uint4 w4 = {pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]};
+            const s16x8 b = __builtin_bit_cast(s16x8, w4);
 #pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
+            for (int db = 0; db < S::DBLK; ++db) {
                 const uint16_t *base = vt + 16 * kc * VP + v_rd[db];
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
                 const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
                 const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                oacc[db] = T::mfma32(a, pk[kc], oacc[db]);
+                oacc[db] = T::mfma32(a, b, oacc[db]);
             }
         }
     };
@@ -368,8 +332,40 @@ void prefill_fwd_kernel(PrefillParams p)
     // flight from global memory during the iteration.  Past the last tile the
     // buffer resources have zero extent, so those loads fetch nothing and
     // return zeros; the extra S block of the last iteration is discarded.
+    // Row max of a masked S^T tile, taken before the tile's exponentials: the
+    // running max moves only past the threshold, and then O and l are
+    // rescaled (a wave-uniform branch that is rarely taken after the first
+    // tile).
+    auto row_max_update = [&](const f32x16 (&sacc)[2]) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
+        mx = max_halves(mx);
+        const float cand = mx * c;
+        const float m_new = cand > m_run + kRescaleThreshold ? cand : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
+        m_run = m_new;
+        l_run0 *= alpha;
+        l_run1 *= alpha;
+        if (rescale) {
+#pragma unroll
+            for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+    };
+
+    // Software pipeline: iteration t computes S for tile t+1 (MFMA) while it
+    // runs the exponentials of tile t (VALU), then O += V_t P_t, then the row
+    // max of tile t+1.  K runs one tile ahead of V in the LDS double buffers;
+    // tile t+2 of K and t+1 of V are in flight from global memory during the
+    // iteration.  Past the last tile the buffer resources have zero extent, so
+    // those loads fetch nothing and return zeros; the extra S block of the
+    // last iteration is discarded.
     f32x16 sa[2], sb[2];
-    s16x8 pk[4];
     if (ntiles > 0) {
         load_k(0, P0{});
         load_v(0, P0{});
@@ -380,30 +376,55 @@ void prefill_fwd_kernel(PrefillParams p)
         tiles_ready();
         compute_s(P0{}, sa);
         mask_tail(0, sa);
+        row_max_update(sa);
         __syncthreads();   // K buffer 0 is refilled at the start of iteration 0
     }
+
+    constexpr int NS = 2 * S::KSTEPS;   // S MFMAs per tile (two 32-key blocks)
     // par = t % 2: K(t) and V(t) live in buffer par, K(t+1) in buffer 1 - par
-    auto step = [&](int t, auto par, auto npar, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         load_k(t + 2, par);
         load_v(t + 1, npar);
-        compute_s(npar, nxt);
-        float alpha;
-        const bool rescale = softmax(cur, pk, alpha);
-        // interleave the S MFMAs of tile t+1 with the softmax VALU of tile t
+        __builtin_amdgcn_sched_barrier(0);
+
+        // The NS MFMAs of S(t+1) = K(t+1) Q^T, in the order ks outer, kb2
+        // inner (two independent accumulator chains), each K operand read two
+        // MFMAs ahead.  Between consecutive MFMAs sits a slice of the softmax
+        // of tile t: exponentials, 16-bit packing and row sums of its 16 value
+        // pairs.
+        const uint16_t *kt = kbuf(npar);
+        auto kop = [&](int i) {
+            return *reinterpret_cast<const s16x8 *>(kt + 32 * (i & 1) * KP + k_rd[i >> 1]);
+        };
+        s16x8 kq0 = kop(0), kq1 = kop(1), kq2;
+        const f32x16 zero = {};
+        uint32_t pw[16];
 #pragma unroll
-        for (int i = 0; i < 2 * S::KSTEPS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
+        for (int i = 0; i < NS; ++i) {
+            const int ks = i >> 1, kb2 = i & 1;
+            nxt[kb2] = T::mfma32(kq0, qreg[ks], ks == 0 ? zero : nxt[kb2]);
+            kq0 = kq1;
+            if (i + 2 < NS) kq2 = kop(i + 2);
+            kq1 = kq2;
+            const int pb = (16 * i) / NS, pe = (16 * (i + 1)) / NS;
+#pragma unroll
+            for (int pi = pb; pi < pe; ++pi) {
+                const int kb = pi >> 3, r = 2 * (pi & 7);
+                const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], c, -m_run));
+                const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c, -m_run));
+                pw[pi] = pack2<T>(p0, p1);
+                if constexpr (S::ONES_COL < 0) {
+                    if (pi & 1) l_run1 = T::sum2(pw[pi], l_run1);
+                    else l_run0 = T::sum2(pw[pi], l_run0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (rescale) {
-#pragma unroll
-            for (int db = 0; db < S::DBLK; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        pv(par, pw);
+        if (t + 1 < ntiles) {
+            mask_tail(t + 1, nxt);
+            row_max_update(nxt);
         }
-        pv(par, pk);
-        mask_tail(t + 1, nxt);
         store_k(par);
         store_v(npar);
         tiles_ready();
@@ -417,11 +438,11 @@ void prefill_fwd_kernel(PrefillParams p)
     float l_tot;
     if constexpr (S::ONES_COL < 0) {
         const float l_run = l_run0 + l_run1;
-        l_tot = l_run + xor_shfl(l_run, 32);
+        l_tot = l_run + swap_halves(l_run);
     } else {
         // row 72 of O^T = block 2, register 4, lanes 0..31
         const float lv = oacc[2][4];
-        const float other = xor_shfl(lv, 32);
+        const float other = swap_halves(lv);
         l_tot = hi ? other : lv;
     }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
