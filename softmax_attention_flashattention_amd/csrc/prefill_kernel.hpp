@@ -135,6 +135,7 @@ void prefill_fwd_kernel(PrefillParams p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same value, in an SGPR
     const int l32 = lane & 31, hi = lane >> 5;
     const int64_t rs = static_cast<int64_t>(p.num_heads) * D;   // token row stride, elements
     const uint32_t row_bytes = static_cast<uint32_t>(rs * 2);
@@ -217,7 +218,7 @@ void prefill_fwd_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(kbuf(par) + (16 * wave + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
+                    r, (lds_void *)(kbuf(par) + (16 * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
         } else {
 #pragma unroll
             for (int i = 0; i < PER; ++i)
@@ -230,7 +231,7 @@ void prefill_fwd_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(vbuf(par) + (16 * wave + 4 * j) * VP), 16, dv_off,
+                    r, (lds_void *)(vbuf(par) + (16 * wave_s + 4 * j) * VP), 16, dv_off,
                     static_cast<int>(4 * j * row_bytes), 0, 0);
         } else {
 #pragma unroll
@@ -309,7 +310,9 @@ void prefill_fwd_kernel(PrefillParams p)
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
     // O^T += V^T P^T.  kc outer, db inner: consecutive MFMAs are independent.
-    auto pv = [&](auto par, const uint32_t (&pw)[16]) {
+    // Between the MFMAs runs `slice(j)`, a piece of VALU work (the row max of
+    // the next tile).
+    auto pv = [&](auto par, const uint32_t (&pw)[16], auto &&slice) {
         const uint16_t *vt = vbuf(par);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
@@ -322,29 +325,26 @@ void prefill_fwd_kernel(PrefillParams p)
                 const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
                 const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
                 oacc[db] = T::mfma32(a, b, oacc[db]);
+                slice(kc * S::DBLK + db);
             }
         }
     };
 
-    // Software pipeline: iteration t computes S for tile t+1 (MFMA) while it
-    // runs the softmax of tile t (VALU), then O += V_t P_t.  K runs one tile
-    // ahead of V in the LDS double buffers; tile t+2 of K and t+1 of V are in
-    // flight from global memory during the iteration.  Past the last tile the
-    // buffer resources have zero extent, so those loads fetch nothing and
-    // return zeros; the extra S block of the last iteration is discarded.
     // Row max of a masked S^T tile, taken before the tile's exponentials: the
-    // running max moves only past the threshold, and then O and l are
-    // rescaled (a wave-uniform branch that is rarely taken after the first
-    // tile).
-    auto row_max_update = [&](const f32x16 (&sacc)[2]) {
-        float mx = -INFINITY;
+    // running max moves only past the threshold (and only when `valid`), and
+    // then O and l are rescaled (a wave-uniform branch that is rarely taken
+    // after the first tile).
+    auto max_part = [&](const f32x16 (&sacc)[2], int j, int nparts, float mx) {
+        // values j * 32 / nparts .. (j + 1) * 32 / nparts - 1 of this lane
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
+        for (int v = (32 * j) / nparts; v < (32 * (j + 1)) / nparts; ++v)
+            mx = fmaxf(mx, sacc[v >> 4][v & 15]);
+        return mx;
+    };
+    auto max_finish = [&](float mx, bool valid) {
         mx = max_halves(mx);
         const float cand = mx * c;
-        const float m_new = cand > m_run + kRescaleThreshold ? cand : m_run;
+        const float m_new = valid && cand > m_run + kRescaleThreshold ? cand : m_run;
         const float alpha = fast_exp2(m_run - m_new);
         const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
         m_run = m_new;
@@ -376,13 +376,15 @@ void prefill_fwd_kernel(PrefillParams p)
         tiles_ready();
         compute_s(P0{}, sa);
         mask_tail(0, sa);
-        row_max_update(sa);
+        max_finish(max_part(sa, 0, 1, -INFINITY), true);
         __syncthreads();   // K buffer 0 is refilled at the start of iteration 0
     }
 
     constexpr int NS = 2 * S::KSTEPS;   // S MFMAs per tile (two 32-key blocks)
     // par = t % 2: K(t) and V(t) live in buffer par, K(t+1) in buffer 1 - par
-    auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    // masked: whether S(t+1) may be the partial last tile (a branch; kept out
+    // of the main loop so that the exponentials are not moved past it)
+    auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2], auto masked) {
         load_k(t + 2, par);
         load_v(t + 1, npar);
         __builtin_amdgcn_sched_barrier(0);
@@ -414,25 +416,40 @@ void prefill_fwd_kernel(PrefillParams p)
                 const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c, -m_run));
                 pw[pi] = pack2<T>(p0, p1);
                 if constexpr (S::ONES_COL < 0) {
-                    if (pi & 1) l_run1 = T::sum2(pw[pi], l_run1);
-                    else l_run0 = T::sum2(pw[pi], l_run0);
+                    // the empty asm keeps each sum in its slice (otherwise the
+                    // compiler sinks the whole chain to the end of the loop)
+                    if (pi & 1) {
+                        l_run1 = T::sum2(pw[pi], l_run1);
+                        asm volatile("" : "+v"(l_run1));
+                    } else {
+                        l_run0 = T::sum2(pw[pi], l_run0);
+                        asm volatile("" : "+v"(l_run0));
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        pv(par, pw);
-        if (t + 1 < ntiles) {
-            mask_tail(t + 1, nxt);
-            row_max_update(nxt);
-        }
+        if constexpr (decltype(masked)::value) mask_tail(t + 1, nxt);
+        float mx = -INFINITY;
+        pv(par, pw, [&](int j) {
+            mx = max_part(nxt, j, 4 * S::DBLK, mx);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        max_finish(mx, t + 1 < ntiles);
         store_k(par);
         store_v(npar);
         tiles_ready();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, P0{}, P1{}, sa, sb);
-        if (t + 1 < ntiles) step(t + 1, P1{}, P0{}, sb, sa);
+    using Unmasked = std::false_type;
+    using Masked = std::true_type;
+    int t = 0;
+    for (; t + 3 < ntiles; t += 2) {            // S(t+1), S(t+2) are full tiles
+        step(t, P0{}, P1{}, sa, sb, Unmasked{});
+        step(t + 1, P1{}, P0{}, sb, sa, Unmasked{});
     }
+    if (t < ntiles) step(t, P0{}, P1{}, sa, sb, Masked{});
+    if (t + 1 < ntiles) step(t + 1, P1{}, P0{}, sb, sa, Masked{});
+    if (t + 2 < ntiles) step(t + 2, P0{}, P1{}, sa, sb, Masked{});
 
     // ---- epilogue: normalise, round to 16 bits, store rows inside the segment
     float l_tot;
