@@ -313,20 +313,25 @@ void prefill_fwd_kernel(PrefillParams p)
     // Between the MFMAs runs `slice(j)`, a piece of VALU work (the row max of
     // the next tile).
     auto pv = [&](auto par, const uint32_t (&pw)[16], auto &&slice) {
+        constexpr int NPV = 4 * S::DBLK;   // MFMAs, j = kc * DBLK + db
+        constexpr int PD = 3;              // V^T operands read this many MFMAs ahead
         const uint16_t *vt = vbuf(par);
+        auto vop = [&](int j) {
+            const uint16_t *base = vt + 16 * (j / S::DBLK) * VP + v_rd[j % S::DBLK];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
+            return s16x8{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        };
+        s16x8 a[PD + 1];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
+        for (int j = 0; j < PD; ++j) a[j] = vop(j);
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            if (j + PD < NPV) a[(j + PD) % (PD + 1)] = vop(j + PD);
+            const int kc = j / S::DBLK, db = j % S::DBLK;
             const uint4 w4 = {pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]};
-            const s16x8 b = __builtin_bit_cast(s16x8, w4);
-#pragma unroll
-            for (int db = 0; db < S::DBLK; ++db) {
-                const uint16_t *base = vt + 16 * kc * VP + v_rd[db];
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
-                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                oacc[db] = T::mfma32(a, b, oacc[db]);
-                slice(kc * S::DBLK + db);
-            }
+            oacc[db] = T::mfma32(a[j % (PD + 1)], __builtin_bit_cast(s16x8, w4), oacc[db]);
+            slice(j);
         }
     };
 
@@ -390,7 +395,7 @@ void prefill_fwd_kernel(PrefillParams p)
         __builtin_amdgcn_sched_barrier(0);
 
         // The NS MFMAs of S(t+1) = K(t+1) Q^T, in the order ks outer, kb2
-        // inner (two independent accumulator chains), each K operand read two
+        // inner (two independent accumulator chains), each K operand read KD
         // MFMAs ahead.  Between consecutive MFMAs sits a slice of the softmax
         // of tile t: exponentials, 16-bit packing and row sums of its 16 value
         // pairs.
@@ -398,16 +403,17 @@ void prefill_fwd_kernel(PrefillParams p)
         auto kop = [&](int i) {
             return *reinterpret_cast<const s16x8 *>(kt + 32 * (i & 1) * KP + k_rd[i >> 1]);
         };
-        s16x8 kq0 = kop(0), kq1 = kop(1), kq2;
+        constexpr int KD = 3;   // K operands read this many MFMAs ahead
+        s16x8 kq[KD + 1];
+#pragma unroll
+        for (int i = 0; i < KD; ++i) kq[i] = kop(i);
         const f32x16 zero = {};
         uint32_t pw[16];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int ks = i >> 1, kb2 = i & 1;
-            nxt[kb2] = T::mfma32(kq0, qreg[ks], ks == 0 ? zero : nxt[kb2]);
-            kq0 = kq1;
-            if (i + 2 < NS) kq2 = kop(i + 2);
-            kq1 = kq2;
+            if (i + KD < NS) kq[(i + KD) % (KD + 1)] = kop(i + KD);
+            nxt[kb2] = T::mfma32(kq[i % (KD + 1)], qreg[ks], ks == 0 ? zero : nxt[kb2]);
             const int pb = (16 * i) / NS, pe = (16 * (i + 1)) / NS;
 #pragma unroll
             for (int pi = pb; pi < pe; ++pi) {
