@@ -20,7 +20,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ER
 template <int D, typename T>
 int launch_prefill(const attn::PrefillParams &p, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(grid), dim3(attn::kPrefillThreads), 0,
+    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(grid), dim3(attn::prefill_threads<D>()), 0,
                        stream, p);
     return launch_status();
 }
@@ -94,7 +94,8 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
         !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
         return ATTN_ERR_INVALID_ARG;
 
-    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBM - 1) / attn::kPrefillBM;
+    const int64_t bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
+    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
     const int64_t per_xcd = (work + 7) / 8;
     if (per_xcd * 8 > INT32_MAX) return ATTN_ERR_INVALID_ARG;

@@ -5,8 +5,8 @@
 // Implementation) as a tiled online softmax: the full score matrix is never
 // formed.
 //
-// Work decomposition.  One workgroup (4 waves) owns a tile of BM = 128 query
-// rows of one (sequence, head); each wave owns 32 of those rows.  The
+// Work decomposition.  One workgroup of 4 waves owns a tile of BM = 128
+// query rows of one (sequence, head); each wave owns 32 of those rows.  The
 // workgroup streams the sequence's keys and values in tiles of BN = 64 rows
 // through double-buffered LDS.  For head_dim 128 the tiles go from global
 // memory straight into LDS (buffer loads with the LDS destination bit), laid
@@ -62,6 +62,7 @@ template <> struct PrefillShape<128> {
     static constexpr int KPITCH = 128;  // unpadded rows; chunks XOR-swizzled
     static constexpr int VPITCH = 128;
     static constexpr int ONES_COL = -1;
+    static constexpr int WAVES = 4;   // 8 measured slower: its waves move in lockstep
 };
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
@@ -70,11 +71,14 @@ template <> struct PrefillShape<72> {
     static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
+    static constexpr int WAVES = 4;
 };
 
-constexpr int kPrefillBM = 128;
 constexpr int kPrefillBN = 64;
-constexpr int kPrefillThreads = 256;
+// Workgroup size: WAVES waves of 32 query rows each (BM = 32 WAVES rows).
+template <int D> constexpr int prefill_waves() { return PrefillShape<D>::WAVES; }
+template <int D> constexpr int prefill_bm() { return 32 * prefill_waves<D>(); }
+template <int D> constexpr int prefill_threads() { return 64 * prefill_waves<D>(); }
 
 // Rescaling threshold (log2 units) of the lazy online softmax: the running
 // max is raised, and O, l rescaled, only when some row's new max exceeds it by
@@ -85,13 +89,15 @@ constexpr float kRescaleThreshold = 8.0f;
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D, typename T>
-__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_fwd_kernel(PrefillParams p)
 {
+    constexpr int kPrefillThreads = prefill_threads<D>();
+    constexpr int WAVES = prefill_waves<D>();
     using S = PrefillShape<D>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    constexpr int BM = kPrefillBM, BN = kPrefillBN;
+    constexpr int BM = prefill_bm<D>(), BN = kPrefillBN;
     constexpr int KP = S::KPITCH, VP = S::VPITCH;
     constexpr int CH = D / 8;                      // 16-byte chunks per row
     constexpr int NCH = BN * CH;                   // chunks per K (or V) tile
@@ -181,9 +187,14 @@ void prefill_fwd_kernel(PrefillParams p)
         return rows > 0 ? static_cast<uint32_t>(rows - 1) * row_bytes + D * 2u : 0u;
     };
 
-    // Direct path (head_dim 128): instruction j of wave w fills LDS rows
-    // 16 w + 4 j .. +3 (1 KiB, lane i -> bytes 16 i .. 16 i + 15).  Row R keeps
+    // Direct path (head_dim 128): a tile is 16 DMA instructions of 1 KiB
+    // (4 rows; lane i -> bytes 16 i .. 16 i + 15); instruction j of wave w
+    // fills LDS rows RW w + 4 j .. +3, RW = 64 / WAVES.  Row R keeps
     // logical chunk c at position c ^ (R % 16) for K and c ^ 4 (R % 4) for V.
+    constexpr int DJ = 16 / WAVES;      // DMA instructions per wave per tile
+    constexpr int RW = 64 / WAVES;      // tile rows per wave
+    // (fixed size: a local array sized by a template-dependent constant here
+    // makes hipcc drop the kernel's host launch stub for head_dim 128)
     uint32_t dk_off[4] = {0u, 0u, 0u, 0u};
     uint32_t dv_off = 0u;
     // Staged path (head_dim 72): thread chunks through registers.
@@ -192,11 +203,11 @@ void prefill_fwd_kernel(PrefillParams p)
     if constexpr (DIRECT) {
         const int rsub = lane >> 4, pos = lane & 15;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int R = 16 * wave + 4 * j + rsub;
+        for (int j = 0; j < DJ; ++j) {
+            const int R = RW * wave + 4 * j + rsub;
             dk_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (R & 15));
         }
-        dv_off = static_cast<uint32_t>(16 * wave + rsub) * row_bytes +
+        dv_off = static_cast<uint32_t>(RW * wave + rsub) * row_bytes +
                  16u * static_cast<uint32_t>(pos ^ (4 * (rsub & 3)));
     } else {
 #pragma unroll
@@ -216,9 +227,9 @@ void prefill_fwd_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t r = make_rsrc(k_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
         if constexpr (DIRECT) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < DJ; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(kbuf(par) + (16 * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
+                    r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
         } else {
 #pragma unroll
             for (int i = 0; i < PER; ++i)
@@ -229,9 +240,9 @@ void prefill_fwd_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t r = make_rsrc(v_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
         if constexpr (DIRECT) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < DJ; ++j)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(vbuf(par) + (16 * wave_s + 4 * j) * VP), 16, dv_off,
+                    r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
                     static_cast<int>(4 * j * row_bytes), 0, 0);
         } else {
 #pragma unroll
