@@ -100,7 +100,7 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v,
  *  block_tables   [num_seqs, max_blocks_per_seq] int32; only the first
  *                 ceil(seq_lens[s] / block_size) entries of a row are read
  *  seq_lens       [num_seqs] int32; seq_lens[s] <= 0 gives an all-zero row
- *  head_size      128 (others return ATTN_ERR_UNSUPPORTED)
+ *  head_size      128 or 256 (others return ATTN_ERR_UNSUPPORTED)
  *  block_size     16 (others return ATTN_ERR_UNSUPPORTED)
  *  num_query_heads % num_kv_heads must be 0; the group size
  *                 num_query_heads / num_kv_heads must be at most 16

@@ -25,27 +25,34 @@ int launch_prefill(const attn::PrefillParams &p, int grid, hipStream_t stream)
     return launch_status();
 }
 
-template <typename T, int GMAX>
+template <typename T, int D, int GMAX>
 int launch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((attn::decode_partition_kernel<T, GMAX>), dim3(static_cast<unsigned>(grid)),
-                       dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((attn::decode_partition_kernel<T, D, GMAX>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::kDecodeThreads), 0, stream, p);
     int rc = launch_status();
     if (rc != ATTN_OK || p.num_parts == 1) return rc;
-    hipLaunchKernelGGL((attn::decode_merge_kernel<T>),
+    hipLaunchKernelGGL((attn::decode_merge_kernel<T, D>),
                        dim3(static_cast<unsigned>(static_cast<int64_t>(p.num_seqs) * p.Hq)), dim3(64), 0,
                        stream, p);
     return launch_status();
 }
 
-template <typename T>
-int dispatch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
+template <typename T, int D>
+int dispatch_decode_g(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
 {
-    if (p.G <= 1) return launch_decode<T, 1>(p, grid, stream);
-    if (p.G <= 2) return launch_decode<T, 2>(p, grid, stream);
-    if (p.G <= 4) return launch_decode<T, 4>(p, grid, stream);
-    if (p.G <= 8) return launch_decode<T, 8>(p, grid, stream);
-    return launch_decode<T, 16>(p, grid, stream);
+    if (p.G <= 1) return launch_decode<T, D, 1>(p, grid, stream);
+    if (p.G <= 2) return launch_decode<T, D, 2>(p, grid, stream);
+    if (p.G <= 4) return launch_decode<T, D, 4>(p, grid, stream);
+    if (p.G <= 8) return launch_decode<T, D, 8>(p, grid, stream);
+    return launch_decode<T, D, 16>(p, grid, stream);
+}
+
+template <typename T>
+int dispatch_decode(const attn::DecodeParams &p, int head_size, int64_t grid, hipStream_t stream)
+{
+    return head_size == 128 ? dispatch_decode_g<T, 128>(p, grid, stream)
+                            : dispatch_decode_g<T, 256>(p, grid, stream);
 }
 
 int partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size, int *part_blocks)
@@ -157,7 +164,7 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
     if (num_query_heads % num_kv_heads) return ATTN_ERR_INVALID_ARG;
     if (head_size % 8) return ATTN_ERR_INVALID_ARG;
     if (partition_size % block_size) return ATTN_ERR_INVALID_ARG;
-    if (head_size != attn::kDecodeD || block_size != attn::kDecodeBS) return ATTN_ERR_UNSUPPORTED;
+    if ((head_size != 128 && head_size != 256) || block_size != attn::kDecodeBS) return ATTN_ERR_UNSUPPORTED;
     const int G = num_query_heads / num_kv_heads;
     if (G > 16) return ATTN_ERR_UNSUPPORTED;
     if (num_seqs == 0) return ATTN_OK;
@@ -203,8 +210,8 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
     p.num_parts = np;
     p.scale_log2e = scale * attn::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, grid, s)
-                                    : dispatch_decode<attn::Fp16>(p, grid, s);
+    return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, head_size, grid, s)
+                                    : dispatch_decode<attn::Fp16>(p, head_size, grid, s);
 }
 
 }  // extern "C"

@@ -7,34 +7,41 @@
 // Generation):
 //   token t  -> physical block block_tables[s][t / 16], slot t % 16
 //   K cache  [num_blocks, Hkv, D/8, 16, 8]: one (block, kv head) is a
-//            contiguous 4 KiB chunk laid out [D/8][16 tokens][8 dims]
+//            contiguous chunk laid out [D/8][16 tokens][8 dims]
 //   V cache  [num_blocks, Hkv, D, 16]: one (block, kv head) is a contiguous
-//            4 KiB chunk laid out [D][16 tokens]
+//            chunk laid out [D][16 tokens]
 //   query head hq reads KV head hq / G, G = Hq / Hkv.
 //
 // The operator is bound by HBM bandwidth, so the kernel is shaped around the
-// loads: one wave owns one (sequence, KV head, context partition) and serves
-// all G query heads of that KV head from a single read of each K/V chunk.  A
-// chunk of four blocks (64 tokens) is read with 32 independent 16-byte loads
-// per lane issued back to back; lane l holds, for each block,
-//   K: 32 dims (dim groups l/16 + 4c, c = 0..3) of token l % 16
-//   V: dims 32c + l/2 (c = 0..3), tokens 8 (l % 2) .. +7.
-// Scores need a 4-lane reduction (xor 16, 32); the softmax weights move from
-// the token-owning lanes to the dim-owning lanes through LDS.
+// loads.  A workgroup of four waves owns one (sequence, KV head, context
+// partition) and serves all G query heads of that KV head from a single read
+// of each K/V chunk.  The partition's blocks are dealt to the waves round
+// robin; a wave reads a block's K and V chunks with D/32 + D/32 independent
+// 16-byte loads per lane (the next block's loads are issued before the
+// current one is used) and keeps its own online softmax.  Lane l holds, for
+// each block,
+//   K: dims 8 (4 c + l / 16) .. +7 of token l % 16   (c = 0 .. D/32 - 1)
+//   V: dim 32 c + l / 2 of tokens 8 (l % 2) .. +7.
+// Both dot products run on v_dot2 (two 16-bit products summed into fp32):
+// q K^T with the 16-bit query, P V with the weights rounded to the 16-bit
+// type (like the P operand of the prefill kernel).  Scores need a 4-lane
+// reduction; the weights move from the token-owning lanes to the dim-owning
+// lanes through LDS.  At the end the four waves' (max, sum, partial output)
+// are merged through LDS.
 //
-// Split-K: a context longer than one partition is split over several waves;
-// each writes (running max m in the log2 domain, sum l, unnormalised output
-// o) to the workspace and decode_merge_kernel combines them:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Split-K: a context longer than one partition is split over several
+// workgroups; each writes (running max m in the log2 domain, sum l,
+// unnormalised output o) to the workspace and decode_merge_kernel combines
+// them:  M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace attn {
 
-constexpr int kDecodeD = 128;
 constexpr int kDecodeBS = 16;
-constexpr int kDecodeChunkBlocks = 4;
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
 struct DecodeParams {
     const uint16_t *query, *k_cache, *v_cache;
@@ -49,23 +56,20 @@ struct DecodeParams {
     float scale_log2e;
 };
 
-__device__ __forceinline__ float lo16f_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi16f_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <typename T>
-__device__ __forceinline__ float elem16(const uint4 &v, int e) {
-    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-    return T::to_f32(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu)));
-}
-
-template <typename T, int GMAX>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
+template <typename T, int D, int GMAX>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeParams p)
 {
-    constexpr int D = kDecodeD, BS = kDecodeBS, NB = kDecodeChunkBlocks;
-    __shared__ __attribute__((aligned(16))) float q_lds[GMAX][D];
-    __shared__ __attribute__((aligned(16))) float p_lds[GMAX][NB][BS];
+    constexpr int BS = kDecodeBS, NW = kDecodeWaves;
+    constexpr int NC = D / 32;          // 16-byte loads per lane per block, for K and for V
+    constexpr int CHUNK = D * BS;       // elements of one (block, kv head) chunk
+    __shared__ __attribute__((aligned(16))) uint32_t q_lds[GMAX][D / 2];   // 16-bit pairs
+    __shared__ __attribute__((aligned(16))) float p_lds[NW][GMAX][BS];
+    __shared__ float m_lds[NW][GMAX], l_lds[NW][GMAX];
+    __shared__ __attribute__((aligned(16))) float o_lds[NW][GMAX][D];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int id = blockIdx.x;
     const int part = id % p.num_parts;
     id /= p.num_parts;
@@ -80,155 +84,169 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
     const int t_end = L < t_begin + p.part_blocks * BS ? L : t_begin + p.part_blocks * BS;
 
     if (t_end <= t_begin) {
-        // No tokens here.  With one partition the row is final: zeros.  With
+        // No tokens here.  With one partition the rows are final: zeros.  With
         // several, the merge kernel skips partitions past the context.
-        if (p.num_parts == 1) {
-            for (int g = 0; g < G; ++g) {
-                uint16_t *o = p.out + (static_cast<int64_t>(s) * p.Hq + hq0 + g) * D;
-                o[lane] = 0;
-                o[lane + 64] = 0;
-            }
-        }
+        if (p.num_parts == 1)
+            for (int i = tid; i < G * D; i += kDecodeThreads)
+                p.out[(static_cast<int64_t>(s) * p.Hq + hq0) * D + i] = 0;
         return;
     }
 
-    // q scaled into the log2 domain, fp32, in LDS
-    for (int i = lane; i < G * D; i += 64) {
-        const int g = i / D, d = i % D;
-        q_lds[g][d] = T::to_f32(p.query[(static_cast<int64_t>(s) * p.Hq + hq0 + g) * D + d]) *
-                      p.scale_log2e;
+    // the G query rows of this KV head, as 16-bit pairs
+    {
+        const uint32_t *qsrc = reinterpret_cast<const uint32_t *>(
+            p.query + (static_cast<int64_t>(s) * p.Hq + hq0) * D);
+        for (int i = tid; i < G * D / 2; i += kDecodeThreads) q_lds[i / (D / 2)][i % (D / 2)] = qsrc[i];
     }
     __syncthreads();
 
-    float m_run[GMAX], l_run[GMAX], acc[GMAX][4];
+    float m_run[GMAX], l_run[GMAX], acc[GMAX][NC];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
         m_run[g] = -INFINITY;
         l_run[g] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[g][c] = 0.f;
+        for (int c = 0; c < NC; ++c) acc[g][c] = 0.f;
     }
 
     const int blk_begin = t_begin / BS;
     const int blk_end = (t_end + BS - 1) / BS;
     const int32_t *bt_row = p.block_tables + static_cast<int64_t>(s) * p.maxb;
-    const int kgrp = lane >> 4;     // K: dim group within a 1 KiB slice
-    const int vhalf = lane & 1;     // V: which 8 tokens of the row
+    const int kgrp = lane >> 4;        // K: dim group inside a 1 KiB slice
+    const int vhalf = lane & 1;        // V: which 8 tokens of a dim row
+    const float c2 = p.scale_log2e;
 
-    for (int b0 = blk_begin; b0 < blk_end; b0 += NB) {
-        uint4 kr[NB][4], vr[NB][4];
-        bool ok[NB];
+    auto load_block = [&](int jb, uint4 (&kr)[NC], uint4 (&vr)[NC]) -> bool {
+        int64_t phys = -1;
+        if (jb < blk_end) phys = bt_row[jb];
+        const bool ok = phys >= 0 && phys < p.num_blocks;
+        const int64_t base = ok ? (phys * p.Hkv + hk) * CHUNK : 0;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int jb = b0 + j;
-            int64_t phys = -1;
-            if (jb < blk_end) phys = bt_row[jb];
-            ok[j] = phys >= 0 && phys < p.num_blocks;
-            const int64_t base = ok[j] ? (phys * p.Hkv + hk) * (D * BS) : 0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 z = {0u, 0u, 0u, 0u};
-                kr[j][c] = ok[j] ? ld16(p.k_cache + base + c * 512 + lane * 8) : z;
-                vr[j][c] = ok[j] ? ld16(p.v_cache + base + c * 512 + lane * 8) : z;
-            }
+        for (int c = 0; c < NC; ++c) {
+            const uint4 z = {0u, 0u, 0u, 0u};
+            kr[c] = ok ? ld16(p.k_cache + base + c * 512 + lane * 8) : z;
+            vr[c] = ok ? ld16(p.v_cache + base + c * 512 + lane * 8) : z;
         }
+        return ok;
+    };
 
-        // scores of token (lane % 16) of each block, per query head
-        float sc[GMAX][NB];
+    uint4 kr[NC], vr[NC], kn[NC], vn[NC];
+    int jb = blk_begin + wave;
+    bool ok = load_block(jb, kr, vr);
+    for (; jb < blk_end; jb += NW) {
+        const bool ok_next = load_block(jb + NW, kn, vn);   // in flight while this block is used
+        const int tok = jb * BS + (lane & 15);
+        const bool valid = ok && tok < t_end;
+
 #pragma unroll
         for (int g = 0; g < GMAX; ++g) {
             if (g < G) {
+                // score of token lane % 16: partial over this lane's 8 NC dims
+                float dot = 0.f;
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    float dot = 0.f;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float *qv = &q_lds[g][8 * (4 * c + kgrp)];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], elem16<T>(kr[j][c], e), dot);
-                    }
-                    dot += xor_shfl(dot, 16);
-                    dot += xor_shfl(dot, 32);
-                    const int tok = (b0 + j) * BS + (lane & 15);
-                    sc[g][j] = (ok[j] && tok < t_end) ? dot : -INFINITY;
+                for (int c = 0; c < NC; ++c) {
+                    const uint4 qv = *reinterpret_cast<const uint4 *>(&q_lds[g][4 * (4 * c + kgrp)]);
+                    dot = T::dot2(kr[c].x, qv.x, dot);
+                    dot = T::dot2(kr[c].y, qv.y, dot);
+                    dot = T::dot2(kr[c].z, qv.z, dot);
+                    dot = T::dot2(kr[c].w, qv.w, dot);
                 }
-            }
-        }
-
-        // online softmax per query head; weights to LDS for the V pass
+                dot += xor_shfl(dot, 16);
+                dot += swap_halves(dot);
+                const float sc = valid ? dot * c2 : -INFINITY;
+                // online softmax over the block's 16 tokens (lanes 0..15, replicated)
+                float bm = sc;
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g) {
-            if (g < G) {
-                float cm = sc[g][0];
-#pragma unroll
-                for (int j = 1; j < NB; ++j) cm = fmaxf(cm, sc[g][j]);
-#pragma unroll
-                for (int sh = 1; sh < 16; sh <<= 1) cm = fmaxf(cm, xor_shfl(cm, sh));
-                const float m_new = fmaxf(m_run[g], cm);
+                for (int sh = 1; sh < 16; sh <<= 1) bm = fmaxf(bm, xor_shfl(bm, sh));
+                const float m_new = fmaxf(m_run[g], bm);
                 const bool none = m_new == -INFINITY;
                 const float alpha = none ? 1.f : fast_exp2(m_run[g] - m_new);
-                float ps = 0.f;
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const float pj = none ? 0.f : fast_exp2(sc[g][j] - m_new);
-                    ps += pj;
-                    if (lane < 16) p_lds[g][j][lane] = pj;
-                }
+                const float pv = none ? 0.f : fast_exp2(sc - m_new);
+                float ps = pv;
 #pragma unroll
                 for (int sh = 1; sh < 16; sh <<= 1) ps += xor_shfl(ps, sh);
                 l_run[g] = l_run[g] * alpha + ps;
                 m_run[g] = m_new;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[g][c] *= alpha;
+                for (int c = 0; c < NC; ++c) acc[g][c] *= alpha;
+                if (lane < 16) p_lds[wave][g][lane] = pv;
             }
         }
-        __syncthreads();
-
-        // acc[g][c] += sum over this lane's 8 tokens of p * V[token][32c + lane/2]
+        // p_lds is written and read by this wave only: LDS operations of one
+        // wave complete in order
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int g = 0; g < GMAX; ++g) {
             if (g < G) {
+                const float4 pa = *reinterpret_cast<const float4 *>(&p_lds[wave][g][8 * vhalf]);
+                const float4 pb = *reinterpret_cast<const float4 *>(&p_lds[wave][g][8 * vhalf + 4]);
+                const uint32_t w0 = T::pack2(pa.x, pa.y), w1 = T::pack2(pa.z, pa.w);
+                const uint32_t w2 = T::pack2(pb.x, pb.y), w3 = T::pack2(pb.z, pb.w);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const float4 pa = *reinterpret_cast<const float4 *>(&p_lds[g][j][8 * vhalf]);
-                    const float4 pb = *reinterpret_cast<const float4 *>(&p_lds[g][j][8 * vhalf + 4]);
-                    const float pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        float a = acc[g][c];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) a = __builtin_fmaf(pw[e], elem16<T>(vr[j][c], e), a);
-                        acc[g][c] = a;
-                    }
+                for (int c = 0; c < NC; ++c) {
+                    float a = acc[g][c];
+                    a = T::dot2(vr[c].x, w0, a);
+                    a = T::dot2(vr[c].y, w1, a);
+                    a = T::dot2(vr[c].z, w2, a);
+                    a = T::dot2(vr[c].w, w3, a);
+                    acc[g][c] = a;
                 }
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            kr[c] = kn[c];
+            vr[c] = vn[c];
+        }
+        ok = ok_next;
     }
 
     // lanes l and l ^ 1 hold the two 8-token halves of the same dims
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[g][c] += xor_shfl(acc[g][c], 1);
+        for (int c = 0; c < NC; ++c) acc[g][c] += xor_shfl(acc[g][c], 1);
 
-    for (int g = 0; g < G && g < GMAX; ++g) {
+    // merge the four waves through LDS
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+            if (lane == 0) {
+                m_lds[wave][g] = m_run[g];
+                l_lds[wave][g] = l_run[g];
+            }
+            if (vhalf == 0) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) o_lds[wave][g][32 * c + (lane >> 1)] = acc[g][c];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * D; i += kDecodeThreads) {
+        const int g = i / D, d = i % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][g]);
+        float num = 0.f, den = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = m_lds[w][g];
+                const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+                den += sc * l_lds[w][g];
+                num += sc * o_lds[w][g][d];
+            }
+        }
         const int64_t row = static_cast<int64_t>(s) * p.Hq + hq0 + g;
         if (p.num_parts == 1) {
-            const float inv = l_run[g] > 0.f ? 1.f / l_run[g] : 0.f;
-            if (vhalf == 0) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) p.out[row * D + 32 * c + (lane >> 1)] = T::from_f32(acc[g][c] * inv);
-            }
+            p.out[row * D + d] = T::from_f32(den > 0.f ? num / den : 0.f);
         } else {
             const int64_t slot = row * p.num_parts + part;
-            if (vhalf == 0) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) p.ws_o[slot * D + 32 * c + (lane >> 1)] = acc[g][c];
-            }
-            if (lane == 0) {
-                p.ws_ml[slot * 2 + 0] = m_run[g];
-                p.ws_ml[slot * 2 + 1] = l_run[g];
+            p.ws_o[slot * D + d] = num;
+            if (d == 0) {
+                p.ws_ml[slot * 2 + 0] = M;
+                p.ws_ml[slot * 2 + 1] = den;
             }
         }
     }
@@ -236,10 +254,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeParams p)
 
 // One wave per (sequence, query head): log-sum-exp merge of the partitions
 // that hold part of the context.
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 {
-    constexpr int D = kDecodeD, BS = kDecodeBS;
+    constexpr int BS = kDecodeBS;
     const int lane = threadIdx.x;
     const int64_t row = blockIdx.x;  // s * Hq + hq
     const int s = static_cast<int>(row / p.Hq);
@@ -251,20 +269,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p)
 
     float M = -INFINITY;
     for (int i = 0; i < nparts; ++i) M = fmaxf(M, p.ws_ml[(row * p.num_parts + i) * 2]);
-    float den = 0.f, o0 = 0.f, o1 = 0.f;
+    float den = 0.f, o[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
     if (M != -INFINITY) {
         for (int i = 0; i < nparts; ++i) {
             const int64_t slot = row * p.num_parts + i;
             const float m = p.ws_ml[slot * 2];
             const float w = m == -INFINITY ? 0.f : fast_exp2(m - M);
             den += w * p.ws_ml[slot * 2 + 1];
-            o0 += w * p.ws_o[slot * D + lane];
-            o1 += w * p.ws_o[slot * D + lane + 64];
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) o[j] += w * p.ws_o[slot * D + lane + 64 * j];
         }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    p.out[row * D + lane] = T::from_f32(o0 * inv);
-    p.out[row * D + lane + 64] = T::from_f32(o1 * inv);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) p.out[row * D + lane + 64 * j] = T::from_f32(o[j] * inv);
 }
 
 }  // namespace attn

@@ -33,12 +33,14 @@ struct Bf16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
-    // acc + lo(w) + hi(w): the two packed 16-bit values of w summed in fp32
-    static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    // acc + a.lo * b.lo + a.hi * b.hi for two packed pairs (v_dot2_f32_bf16)
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                               acc, false);
     }
+    // acc + lo(w) + hi(w): the two packed 16-bit values of w summed in fp32
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc) { return dot2(w, 0x3F803F80u, acc); }
     // two fp32 -> two bf16 (lo first), round to nearest even, one v_cvt_pk_bf16_f32
     static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -62,11 +64,11 @@ struct Fp16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
-    static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        const f16x2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
     }
+    static __device__ __forceinline__ float sum2(uint32_t w, float acc) { return dot2(w, 0x3C003C00u, acc); }
     static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
         typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
         const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};

@@ -91,6 +91,7 @@ def decode(lib, **kw):
 def test_decode_argument_errors(lib):
     assert decode(lib, hkv=3) == INVALID               # 16 % 3 != 0
     assert decode(lib, d=64) == UNSUPPORTED
+    assert decode(lib, d=192) == UNSUPPORTED
     assert decode(lib, d=12) == INVALID                # not a multiple of x = 8
     assert decode(lib, bs=32) == UNSUPPORTED
     assert decode(lib, hq=34, hkv=2) == UNSUPPORTED    # group of 17

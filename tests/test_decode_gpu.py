@@ -116,3 +116,16 @@ def test_scaled_values_tighten_the_floor():
 def test_runs_are_bitwise_deterministic():
     inp = gen.decode_inputs(16, 700, 8, 2, 128, seed=71)
     assert torch.equal(run(inp, 64).cpu(), run(inp, 64).cpu())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("S,L,Hq,Hkv,lens", [
+    (1, 128, 16, 2, None),                        # decode Shapes table row 1
+    (5, 300, 8, 8, [300, 1, 0, 17, 256]),
+    (3, 700, 32, 4, [700, 64, 1]),
+])
+def test_head_size_256(dtype, S, L, Hq, Hkv, lens):
+    inp = gen.decode_inputs(S, L, Hq, Hkv, 256, seed=S * L + Hq, dtype=dtype, seq_lens=lens)
+    full_check(inp, f"D=256 {dtype} {S}x{L} Hq={Hq} Hkv={Hkv}")
+    if L > 256:
+        full_check(inp, f"D=256 split {dtype}", partition_size=128)
