@@ -25,8 +25,9 @@
 // Both dot products run on v_dot2 (two 16-bit products summed into fp32):
 // q K^T with the 16-bit query, P V with the weights rounded to the 16-bit
 // type (like the P operand of the prefill kernel).  Scores need a 4-lane
-// reduction; the weights move from the token-owning lanes to the dim-owning
-// lanes through LDS.  At the end the four waves' (max, sum, partial output)
+// reduction (v_permlane16/32_swap) and the block max and sum a 16-lane one
+// (DPP), all in VALU; the weights move from the token-owning lanes to the
+// dim-owning lanes through LDS.  At the end the four waves' (max, sum, partial output)
 // are merged through LDS.
 //
 // Split-K: a context longer than one partition is split over several
@@ -92,14 +93,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
         return;
     }
 
-    // the G query rows of this KV head, as 16-bit pairs
-    {
-        const uint32_t *qsrc = reinterpret_cast<const uint32_t *>(
-            p.query + (static_cast<int64_t>(s) * p.Hq + hq0) * D);
-        for (int i = tid; i < G * D / 2; i += kDecodeThreads) q_lds[i / (D / 2)][i % (D / 2)] = qsrc[i];
-    }
-    __syncthreads();
-
     float m_run[GMAX], l_run[GMAX], acc[GMAX][NC];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
@@ -130,9 +123,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
         return ok;
     };
 
+    // the first block's loads go out before anything else waits
     uint4 kr[NC], vr[NC], kn[NC], vn[NC];
     int jb = blk_begin + wave;
     bool ok = load_block(jb, kr, vr);
+
+    // the G query rows of this KV head, as 16-bit pairs
+    {
+        const uint32_t *qsrc = reinterpret_cast<const uint32_t *>(
+            p.query + (static_cast<int64_t>(s) * p.Hq + hq0) * D);
+        for (int i = tid; i < G * D / 2; i += kDecodeThreads) q_lds[i / (D / 2)][i % (D / 2)] = qsrc[i];
+    }
+    __syncthreads();
     for (; jb < blk_end; jb += NW) {
         const bool ok_next = load_block(jb + NW, kn, vn);   // in flight while this block is used
         const int tok = jb * BS + (lane & 15);
@@ -151,20 +153,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
                     dot = T::dot2(kr[c].z, qv.z, dot);
                     dot = T::dot2(kr[c].w, qv.w, dot);
                 }
-                dot += xor_shfl(dot, 16);
-                dot += swap_halves(dot);
+                dot = sum_xor16(dot);
+                dot = sum_xor32(dot);
                 const float sc = valid ? dot * c2 : -INFINITY;
                 // online softmax over the block's 16 tokens (lanes 0..15, replicated)
-                float bm = sc;
-#pragma unroll
-                for (int sh = 1; sh < 16; sh <<= 1) bm = fmaxf(bm, xor_shfl(bm, sh));
+                const float bm = row16_max(sc);
                 const float m_new = fmaxf(m_run[g], bm);
                 const bool none = m_new == -INFINITY;
                 const float alpha = none ? 1.f : fast_exp2(m_run[g] - m_new);
                 const float pv = none ? 0.f : fast_exp2(sc - m_new);
-                float ps = pv;
-#pragma unroll
-                for (int sh = 1; sh < 16; sh <<= 1) ps += xor_shfl(ps, sh);
+                const float ps = row16_sum(pv);
                 l_run[g] = l_run[g] * alpha + ps;
                 m_run[g] = m_new;
 #pragma unroll
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[g][c] += xor_shfl(acc[g][c], 1);
+        for (int c = 0; c < NC; ++c) acc[g][c] += dpp_mov<kDppXor1>(acc[g][c]);
 
     // merge the four waves through LDS
 #pragma unroll

@@ -103,6 +103,41 @@ __device__ __forceinline__ float swap_halves(float v) {
     // r[0]: lanes 32..63 now hold lanes 0..31; r[1]: lanes 0..31 now hold lanes 32..63
     return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
 }
+// v + (value of lane l ^ 32), the same bits in both lanes
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v + (value of lane l ^ 16) (v_permlane16_swap exchanges rows 0<->1, 2<->3)
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// DPP moves inside rows of 16 lanes (every source lane is in the row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within each half row
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within the row
+// Reductions over the 16 lanes of each row; every lane of the row gets the
+// same bits (each step combines two equal partial results commutatively).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<kDppXor1>(v));
+    v = fmaxf(v, dpp_mov<kDppXor2>(v));
+    v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+    return fmaxf(v, dpp_mov<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<kDppXor1>(v);
+    v += dpp_mov<kDppXor2>(v);
+    v += dpp_mov<kDppHalfMirror>(v);
+    return v + dpp_mov<kDppMirror>(v);
+}
+
 // max(v, value of lane l ^ 32)
 __device__ __forceinline__ float max_halves(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
