@@ -10,6 +10,9 @@ row 0).  Inputs are seeded standard-normal bf16, resident in HBM before the
 timed region.  Each call is bracketed by HIP events on the stream it is
 launched on; the decode inputs rotate over several copies (more bytes than
 the 256 MB Infinity Cache) so every decode call reads HBM, not the cache.
+The decode roofline figure comes from the same decode calls issued back to
+back after the step loop (a lone 26-us call's event pair would also time its
+dispatch).
 
 Printed: one JSON line with prefill TFLOP/s (the headline value), decode
 GB/s, both against MI355X roofline peaks, and the CPU oracle's rate on a
@@ -123,6 +126,55 @@ def copy_reference(torch, dev, args):
                       "GB/s (read + write)": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def summarize_counters(pmc_dir):
+    """Turns four rocprofv3 --pmc runs into profiles/hbm_traffic.json: HBM bytes
+    per launch of each kernel, FETCH_SIZE and WRITE_SIZE each scaled by what the
+    same counter reads for a plain 1 GiB copy (the --only copy run).
+
+    Expected layout (the -d/-o names of the four runs):
+      <pmc_dir>/f/f_counter_collection.csv    FETCH_SIZE, default bench step
+      <pmc_dir>/w/w_counter_collection.csv    WRITE_SIZE, default bench step
+      <pmc_dir>/cf/cf_counter_collection.csv  FETCH_SIZE, --only copy
+      <pmc_dir>/cw/cw_counter_collection.csv  WRITE_SIZE, --only copy
+    """
+    import csv
+    import collections
+
+    def per_kernel(name):
+        path = os.path.join(pmc_dir, name, f"{name}_counter_collection.csv")
+        vals = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel("f"), per_kernel("w")
+    cf, cw = per_kernel("cf"), per_kernel("cw")
+    copy_kib = (1 << 30) / 1024.0
+    copy_kernel = max(cf, key=cf.get)            # the 1 GiB copy dominates
+    fetch_scale = copy_kib / cf[copy_kernel]
+    write_scale = copy_kib / cw[max(cw, key=cw.get)]
+    out = {"_note": ("HBM bytes per launch = FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale "
+                     "(KiB -> bytes); scales from a plain 1 GiB device copy"),
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+           "copy_kernel": copy_kernel}
+    src_hash = kernel_source_hash(KERNEL_SOURCES)
+    for prefix in ("prefill_fwd_kernel", "decode_partition_kernel"):
+        names = [k for k in fetch if prefix in k]
+        if not names:
+            continue
+        k = names[0]
+        rd = fetch[k] * fetch_scale * 1024.0
+        wr = write.get(k, 0.0) * write_scale * 1024.0
+        out[prefix] = {"kernel": k, "source_hash": src_hash, "read_bytes": round(rd),
+                       "write_bytes": round(wr), "bytes_per_launch": round(rd + wr)}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,12 +182,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate", type=int, default=8,
                     help="decode input copies cycled through (8 x 138 MB > 256 MB cache)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU work for the oracle baseline (0 skips it)")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one part alone (for profiling); 'copy' times a plain 1 GiB "
                          "device-to-device copy, the reference for HBM counter scaling")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
+                    help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
+                         "(no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the kernels run on a single GPU and no multi-GPU path is built)", file=sys.stderr)
@@ -202,7 +259,21 @@ def main():
     pre_ms = sorted(a.elapsed_time(b) for a, b, _, _ in ev)
     dec_ms = sorted(c.elapsed_time(d) for _, _, c, d in ev)
     pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_step_avg = sum(dec_ms) / len(dec_ms)
+    # Decode calls are short enough (tens of microseconds) that a lone call's
+    # event pair also times its dispatch; its per-launch figure comes from the
+    # same calls issued back to back (still rotating the input copies).
+    dec_avg = dec_step_avg
+    if do_decode:
+        reps = 4 * args.steps
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            decode_call(i)
+        b.record()
+        torch.cuda.synchronize()
+        dec_avg = a.elapsed_time(b) / reps
     tflops = flops / (pre_avg * 1e-3) / 1e12 if do_prefill else 0.0
     gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_decode else 0.0
 
@@ -246,7 +317,8 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
                 "kernel": "decode_partition_kernel<bf16, 1>",
                 "bytes_per_launch": dbytes, "avg_launch_us": round(dec_avg * 1e3, 3),
-                "min_launch_us": round(dec_ms[0] * 1e3, 3),
+                "avg_in_step_us": round(dec_step_avg * 1e3, 3),
+                "min_in_step_us": round(dec_ms[0] * 1e3, 3),
             },
         },
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
