@@ -187,6 +187,10 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one part alone (for profiling); 'copy' times a plain 1 GiB "
                          "device-to-device copy, the reference for HBM counter scaling")
+    ap.add_argument("--prefill-workload", default=PREFILL,
+                    choices=[k for k in ("prefill_s276_h4_d72", "prefill_s8136_h16_d72",
+                                         "prefill_s16742_h32_d128", "prefill_s65556_h16_d72")],
+                    help="prefill workload of the step (default: the head_dim-128 roofline case)")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
                          "(no GPU needed)")
@@ -208,7 +212,8 @@ def main():
     if args.only == "copy":
         return copy_reference(torch, dev, args)
 
-    p_host = gen.workload_inputs(PREFILL)
+    p_name = args.prefill_workload
+    p_host = gen.workload_inputs(p_name)
     p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p_host.items()}
     p_out = torch.empty_like(p["q"])
     flops = prefill_flops(p_host)
@@ -278,7 +283,7 @@ def main():
     gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_decode else 0.0
 
     src_hash = kernel_source_hash(KERNEL_SOURCES)
-    pre_traffic = profiled_traffic("prefill_fwd_kernel", src_hash)
+    pre_traffic = profiled_traffic("prefill_fwd_kernel", src_hash) if p_name == PREFILL else None
     dec_traffic = profiled_traffic("decode_partition_kernel", src_hash)
 
     result = {
@@ -295,8 +300,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{PREFILL} + {DECODE}",
-            "prefill": {"seq_lens": [16742], "num_heads": 32, "head_dim": 128,
+            "workload": f"{p_name} + {DECODE}",
+            "prefill": {"seq_lens": [int(p_host["max_seqlen_q"])],
+                        "num_heads": int(p_host["q"].shape[1]),
+                        "head_dim": int(p_host["q"].shape[2]),
                         "scale": "head_dim^-0.5", "causal": False},
             "decode": {"num_seqs": 256, "ctx_len": 64, "num_query_heads": 16,
                        "num_kv_heads": 16, "head_size": 128, "block_size": 16,
@@ -306,7 +313,7 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": pre_traffic,
-            "kernel": "prefill_fwd_kernel<128, bf16>",
+            "kernel": f"prefill_fwd_kernel<{int(p_host['q'].shape[2])}, bf16>",
             "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
             "min_launch_ms": round(pre_ms[0], 4),
         },
