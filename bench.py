@@ -216,6 +216,11 @@ def main():
     p_host = gen.workload_inputs(p_name)
     p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in p_host.items()}
     p_out = torch.empty_like(p["q"])
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    p_ws = torch.empty(attn_varlen_fwd_workspace_size(p_host["cu_seqlens_q"].numel() - 1,
+                                                      p_host["max_seqlen_q"], p_host["q"].shape[1],
+                                                      p_host["q"].shape[2]),
+                       dtype=torch.uint8, device=dev)
     flops = prefill_flops(p_host)
 
     d_host = gen.workload_inputs(DECODE)
@@ -227,7 +232,7 @@ def main():
 
     def prefill_call():
         attn_varlen_fwd(p["q"], p["k"], p["v"], p["cu_seqlens_q"], p["cu_seqlens_k"],
-                        max_seqlen_q=p["max_seqlen_q"], out=p_out)
+                        max_seqlen_q=p["max_seqlen_q"], out=p_out, workspace=p_ws)
 
     def decode_call(i):
         c = d_copies[i % len(d_copies)]

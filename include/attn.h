@@ -71,6 +71,13 @@ typedef enum attn_dtype {
  *                 sizes the grid, so query rows past it are not computed
  *  head_dim       72 or 128 (others return ATTN_ERR_UNSUPPORTED)
  *  scale          finite; the pages use head_dim^-1/2
+ *  workspace      optional device memory, 256-byte aligned, of
+ *                 attn_varlen_fwd_workspace_size(...) bytes.  When the work
+ *                 items would leave the device's last wave of workgroups at
+ *                 most half full, those items are split into key ranges
+ *                 whose partial results go here and a second kernel merges
+ *                 them.  NULL (or too small) runs every item whole: the same
+ *                 result, only slower in that case.
  *  out            [total_q, num_heads, head_dim], dtype.  Only rows inside a
  *                 query segment are written; a sequence with query rows but
  *                 no key rows gets all-zero rows.  Other rows are untouched.
@@ -82,7 +89,16 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v,
                     int32_t num_seqs, int32_t max_seqlen_q,
                     int64_t total_q, int64_t total_k,
                     int32_t num_heads, int32_t head_dim, float scale,
-                    int32_t dtype, void *out, void *stream);
+                    int32_t dtype, void *workspace, size_t workspace_bytes,
+                    void *out, void *stream);
+
+/*
+ * Workspace bytes attn_varlen_fwd can use for these sizes on the current
+ * device (0 when no split applies, on invalid sizes, or when the device
+ * cannot be queried).
+ */
+size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q,
+                                      int32_t num_heads, int32_t head_dim);
 
 /*
  * attn_paged_decode -- single-query attention over a paged KV cache with

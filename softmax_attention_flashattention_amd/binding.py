@@ -48,8 +48,10 @@ def _load():
     lib = ctypes.CDLL(path)
     P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
-    lib.attn_varlen_fwd.argtypes = [P, P, P, P, P, i32, i32, i64, i64, i32, i32, f32, i32, P, P]
+    lib.attn_varlen_fwd.argtypes = [P, P, P, P, P, i32, i32, i64, i64, i32, i32, f32, i32, P, sz, P, P]
     lib.attn_varlen_fwd.restype = ctypes.c_int
+    lib.attn_varlen_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.attn_varlen_fwd_workspace_size.restype = sz
     lib.attn_paged_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32, i32,
                                       i32, P, sz, P, P]
     lib.attn_paged_decode.restype = ctypes.c_int
@@ -89,15 +91,23 @@ def attn_status_string(status):
     return _load().attn_status_string(int(status)).decode()
 
 
+def attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, num_heads, head_dim):
+    """Workspace bytes a varlen prefill call can use on the current device."""
+    return _load().attn_varlen_fwd_workspace_size(int(num_seqs), int(max_seqlen_q),
+                                                  int(num_heads), int(head_dim))
+
+
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scale=None,
-                    out=None):
+                    out=None, workspace=None):
     """Non-causal varlen prefill attention (calls ``attn_varlen_fwd``).
 
     q [total_q, H, D], k/v [total_k, H, D] in bf16 or fp16; cu_seqlens_* int32
     [num_seqs + 1] on the GPU.  ``max_seqlen_q`` defaults to the longest
     query segment (read back from the GPU: a synchronisation).  ``scale``
     defaults to D**-0.5.  Rows outside every query segment of a
-    caller-provided ``out`` are left untouched.
+    caller-provided ``out`` are left untouched.  ``workspace`` (a GPU
+    tensor) defaults to one allocated here of the size the library asks for;
+    an empty tensor runs every work item whole.
     """
     fp16 = (torch.bfloat16, torch.float16)
     _need(q, "q", fp16, 3)
@@ -120,10 +130,15 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
         _need(out, "out", q.dtype, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    if workspace is None:
+        ws_bytes = attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, H, D)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr = _ptr(workspace) if ws_len else None
     rc = _load().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
                                  _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q), total_q,
-                                 k.shape[0], H, D, scale, _DTYPE[q.dtype], _ptr(out),
-                                 _stream(q.device))
+                                 k.shape[0], H, D, scale, _DTYPE[q.dtype], ws_ptr, ws_len,
+                                 _ptr(out), _stream(q.device))
     if rc != 0:
         raise AttnError("attn_varlen_fwd", rc)
     return out

@@ -18,11 +18,60 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 template <int D, typename T>
-int launch_prefill(const attn::PrefillParams &p, int grid, hipStream_t stream)
+int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(grid), dim3(attn::prefill_threads<D>()), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::prefill_threads<D>()), 0, stream, p);
+    int rc = launch_status();
+    if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
+    hipLaunchKernelGGL((attn::prefill_merge_kernel<D, T>), dim3(static_cast<unsigned>(p.total_work - p.whole_work)),
+                       dim3(256), 0, stream, p);
     return launch_status();
+}
+
+// Work items that fit the device at once: compute units x resident
+// workgroups per unit (0 when the runtime cannot tell, e.g. no device).
+template <int D>
+int prefill_slots()
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>,
+                                                     attn::prefill_threads<D>(), 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+// How the work items are launched.  When the last wave of workgroups would
+// be at most half full, its items are split into key ranges (at most 8) that
+// fill it, and a merge kernel combines the ranges.
+struct PrefillPlan {
+    int64_t work = 0, whole = 0, parts = 1, grid = 0;
+    size_t ws_o_bytes = 0, ws_bytes = 0;
+};
+
+PrefillPlan plan_prefill(int64_t work, int slots, int bm, int head_dim)
+{
+    PrefillPlan pl;
+    pl.work = work;
+    const int64_t full = slots > 0 ? work / slots : 0;
+    const int64_t rest = slots > 0 ? work % slots : 0;
+    if (full >= 1 && rest > 0 && 2 * rest <= slots) {
+        pl.parts = slots / rest < 8 ? slots / rest : 8;
+        pl.whole = (full * slots) / 8 * 8;
+    }
+    if (pl.parts < 2) {
+        pl.parts = 1;
+        pl.whole = work / 8 * 8;
+    }
+    pl.grid = pl.whole + (work - pl.whole) * pl.parts;
+    if (pl.parts > 1) {
+        const size_t slots_ws = static_cast<size_t>(work - pl.whole) * pl.parts * bm;
+        pl.ws_o_bytes = (slots_ws * head_dim * sizeof(float) + 255) / 256 * 256;
+        pl.ws_bytes = pl.ws_o_bytes + slots_ws * 2 * sizeof(float);
+    }
+    return pl;
 }
 
 template <typename T, int D, int GMAX>
@@ -83,10 +132,23 @@ const char *attn_status_string(int32_t status)
     }
 }
 
+size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_heads,
+                                      int32_t head_dim)
+{
+    if (num_seqs <= 0 || max_seqlen_q <= 0 || num_heads <= 0) return 0;
+    if (head_dim != 72 && head_dim != 128) return 0;
+    const int bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
+    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
+    const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
+    const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
+    return plan_prefill(work, slots, bm, head_dim).ws_bytes;
+}
+
 int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
                     const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
                     int64_t total_q, int64_t total_k, int32_t num_heads, int32_t head_dim,
-                    float scale, int32_t dtype, void *out, void *stream)
+                    float scale, int32_t dtype, void *workspace, size_t workspace_bytes, void *out,
+                    void *stream)
 {
     if (num_seqs < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || num_heads <= 0 ||
         head_dim <= 0)
@@ -98,14 +160,17 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ATTN_ERR_INVALID_ARG;
     if ((!k || !v) && total_k > 0) return ATTN_ERR_INVALID_ARG;   // k, v may be empty
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
         return ATTN_ERR_INVALID_ARG;
 
-    const int64_t bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
+    const int bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
     const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
-    const int64_t per_xcd = (work + 7) / 8;
-    if (per_xcd * 8 > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+    if (work > INT32_MAX / 8) return ATTN_ERR_INVALID_ARG;
+    const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
+    PrefillPlan pl = plan_prefill(work, slots, bm, head_dim);
+    if (pl.parts > 1 && (!workspace || workspace_bytes < pl.ws_bytes))
+        pl = plan_prefill(work, 0, bm, head_dim);    // no room for the split: run items whole
 
     attn::PrefillParams p;
     p.q = static_cast<const uint16_t *>(q);
@@ -119,16 +184,18 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     p.num_heads = num_heads;
     p.num_qtiles = static_cast<int>(qtiles);
     p.total_work = static_cast<int>(work);
-    p.per_xcd = static_cast<int>(per_xcd);
+    p.whole_work = static_cast<int>(pl.whole);
+    p.split_parts = static_cast<int>(pl.parts);
+    p.ws_o = pl.parts > 1 ? static_cast<float *>(workspace) : nullptr;
+    p.ws_ml = pl.parts > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_o_bytes) : nullptr;
     p.scale_log2e = scale * attn::kLog2e;
-    const int grid = static_cast<int>(per_xcd * 8);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (head_dim == 128)
-        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16>(p, grid, s)
-                                        : launch_prefill<128, attn::Fp16>(p, grid, s);
-    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16>(p, grid, s)
-                                    : launch_prefill<72, attn::Fp16>(p, grid, s);
+        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16>(p, pl.grid, s)
+                                        : launch_prefill<128, attn::Fp16>(p, pl.grid, s);
+    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16>(p, pl.grid, s)
+                                    : launch_prefill<72, attn::Fp16>(p, pl.grid, s);
 }
 
 int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,

@@ -48,9 +48,12 @@ struct PrefillParams {
     uint16_t *out;
     int64_t total_q, total_k;
     int num_heads;
-    int num_qtiles;  // ceil(max_seqlen_q / BM)
-    int total_work;  // num_seqs * num_heads * num_qtiles
-    int per_xcd;     // ceil(total_work / 8)
+    int num_qtiles;   // ceil(max_seqlen_q / BM)
+    int total_work;   // work items: num_seqs * num_heads * num_qtiles
+    int whole_work;   // items [0, whole_work) run whole; a multiple of 8
+    int split_parts;  // items [whole_work, total_work) run as this many key ranges
+    float *ws_o;      // split items: [(item - whole_work) * split_parts + part][BM][D], unnormalised O
+    float *ws_ml;     // split items: [... same slot ...][BM][2]: running max (log2 domain), row sum
     float scale_log2e;
 };
 
@@ -116,12 +119,22 @@ void prefill_fwd_kernel(PrefillParams p)
         if constexpr (decltype(par)::value == 0) return v_lds0; else return v_lds1;
     };
 
-    // XCD-aware work id: hardware hands consecutive workgroups to the 8 XCDs
-    // in turn, so bid -> (bid % 8) * per_xcd + bid / 8 keeps runs of
-    // consecutive work items (same head, neighbouring query tiles, hence the
-    // same K/V stream) on one XCD and its L2.
+    // Work id.  Hardware hands consecutive workgroups to the 8 XCDs in turn,
+    // so for the whole items bid -> (bid % 8) * (whole_work / 8) + bid / 8
+    // keeps runs of consecutive items (same head, neighbouring query tiles,
+    // hence the same K/V stream) on one XCD and its L2.  The items left for
+    // the last, partly filled wave of workgroups are split into key ranges
+    // (`split_parts` workgroups each) so that they fill it.
     const int bid = blockIdx.x;
-    const int w = (bid & 7) * p.per_xcd + (bid >> 3);
+    int w, part = 0, nparts = 1;
+    if (bid < p.whole_work) {
+        w = (bid & 7) * (p.whole_work >> 3) + (bid >> 3);
+    } else {
+        const int j = bid - p.whole_work;
+        nparts = p.split_parts;
+        w = p.whole_work + j / nparts;
+        part = j % nparts;
+    }
     if (w >= p.total_work) return;
     const int qtile = w % p.num_qtiles;
     const int sh = w / p.num_qtiles;
@@ -181,10 +194,13 @@ void prefill_fwd_kernel(PrefillParams p)
     // ---- tile movement.  Each tile gets its own buffer resource whose extent
     // ends at the sequence's last key (zero past the last tile), so rows past
     // the end read as zeros and loads past the last tile fetch nothing.
+    // this workgroup's key tiles [t0, t1)
     const int ntiles = (Sk + BN - 1) / BN;
+    const int t0 = static_cast<int>((static_cast<int64_t>(part) * ntiles) / nparts);
+    const int t1 = static_cast<int>((static_cast<int64_t>(part + 1) * ntiles) / nparts);
     auto tile_bytes = [&](int t) -> uint32_t {
         const int rows = Sk - t * BN < BN ? Sk - t * BN : BN;
-        return rows > 0 ? static_cast<uint32_t>(rows - 1) * row_bytes + D * 2u : 0u;
+        return (rows > 0 && t < t1) ? static_cast<uint32_t>(rows - 1) * row_bytes + D * 2u : 0u;
     };
 
     // Direct path (head_dim 128): a tile is 16 DMA instructions of 1 KiB
@@ -382,22 +398,22 @@ void prefill_fwd_kernel(PrefillParams p)
     // those loads fetch nothing and return zeros; the extra S block of the
     // last iteration is discarded.
     f32x16 sa[2], sb[2];
-    if (ntiles > 0) {
-        load_k(0, P0{});
-        load_v(0, P0{});
+    if (t1 > t0) {
+        load_k(t0, P0{});
+        load_v(t0, P0{});
         store_k(P0{});
         store_v(P0{});
-        load_k(1, P1{});
+        load_k(t0 + 1, P1{});
         store_k(P1{});
         tiles_ready();
         compute_s(P0{}, sa);
-        mask_tail(0, sa);
+        mask_tail(t0, sa);
         max_finish(max_part(sa, 0, 1, -INFINITY), true);
-        __syncthreads();   // K buffer 0 is refilled at the start of iteration 0
+        __syncthreads();   // K buffer 0 is refilled at the start of the first iteration
     }
 
     constexpr int NS = 2 * S::KSTEPS;   // S MFMAs per tile (two 32-key blocks)
-    // par = t % 2: K(t) and V(t) live in buffer par, K(t+1) in buffer 1 - par
+    // par = (t - t0) % 2: K(t) and V(t) live in buffer par, K(t+1) in buffer 1 - par
     // masked: whether S(t+1) may be the partial last tile (a branch; kept out
     // of the main loop so that the exponentials are not moved past it)
     auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2], auto masked) {
@@ -452,21 +468,21 @@ void prefill_fwd_kernel(PrefillParams p)
             mx = max_part(nxt, j, 4 * S::DBLK, mx);
             __builtin_amdgcn_sched_barrier(0);
         });
-        max_finish(mx, t + 1 < ntiles);
+        max_finish(mx, t + 1 < t1);
         store_k(par);
         store_v(npar);
         tiles_ready();
     };
     using Unmasked = std::false_type;
     using Masked = std::true_type;
-    int t = 0;
-    for (; t + 3 < ntiles; t += 2) {            // S(t+1), S(t+2) are full tiles
+    int t = t0;
+    for (; t + 3 < t1; t += 2) {                // S(t+1), S(t+2) are full tiles
         step(t, P0{}, P1{}, sa, sb, Unmasked{});
         step(t + 1, P1{}, P0{}, sb, sa, Unmasked{});
     }
-    if (t < ntiles) step(t, P0{}, P1{}, sa, sb, Masked{});
-    if (t + 1 < ntiles) step(t + 1, P1{}, P0{}, sb, sa, Masked{});
-    if (t + 2 < ntiles) step(t + 2, P0{}, P1{}, sa, sb, Masked{});
+    if (t < t1) step(t, P0{}, P1{}, sa, sb, Masked{});
+    if (t + 1 < t1) step(t + 1, P1{}, P0{}, sb, sa, Masked{});
+    if (t + 2 < t1) step(t + 2, P0{}, P1{}, sa, sb, Masked{});
 
     // ---- epilogue: normalise, round to 16 bits, store rows inside the segment
     float l_tot;
@@ -478,6 +494,27 @@ void prefill_fwd_kernel(PrefillParams p)
         const float lv = oacc[2][4];
         const float other = swap_halves(lv);
         l_tot = hi ? other : lv;
+    }
+    if (nparts > 1) {
+        // a key range of a split item: unnormalised O^T, running max and row
+        // sum to the workspace; prefill_merge_kernel combines the ranges
+        if (qrow < Sq) {
+            const int64_t slot = static_cast<int64_t>(w - p.whole_work) * nparts + part;
+            const int row = 32 * wave + l32;
+            float *o = p.ws_o + (slot * BM + row) * D;
+#pragma unroll
+            for (int db = 0; db < S::DBLK; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = 32 * db + 8 * g4 + 4 * hi;
+                    if (d < D)
+                        *reinterpret_cast<float4 *>(o + d) =
+                            make_float4(oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2],
+                                        oacc[db][4 * g4 + 3]);
+                }
+            if (hi == 0) *reinterpret_cast<float2 *>(p.ws_ml + (slot * BM + row) * 2) = make_float2(m_run, l_tot);
+        }
+        return;
     }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < Sq) {
@@ -495,6 +532,56 @@ void prefill_fwd_kernel(PrefillParams p)
                 }
             }
     }
+}
+
+// Log-sum-exp merge of the key ranges of the split work items: one
+// workgroup per item, two threads per query row (each half of head_dim).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p)
+{
+    constexpr int BM = prefill_bm<D>();
+    static_assert(2 * BM == 256, "two threads per query row");
+    const int w = p.whole_work + blockIdx.x;
+    if (w >= p.total_work) return;
+    const int qtile = w % p.num_qtiles;
+    const int sh = w / p.num_qtiles;
+    const int head = sh % p.num_heads;
+    const int seq = sh / p.num_heads;
+    int64_t qa = p.cu_q[seq], qb = p.cu_q[seq + 1];
+    qa = qa < 0 ? 0 : (qa > p.total_q ? p.total_q : qa);
+    qb = qb < qa ? qa : (qb > p.total_q ? p.total_q : qb);
+    const int Sq = static_cast<int>(qb - qa);
+    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int q = qtile * BM + row;
+    if (q >= Sq) return;
+    const int P = p.split_parts;
+    const int64_t slot0 = static_cast<int64_t>(blockIdx.x) * P;
+
+    float M = -INFINITY;
+    for (int i = 0; i < P; ++i) M = fmaxf(M, p.ws_ml[((slot0 + i) * BM + row) * 2]);
+    constexpr int H2 = D / 2;   // values per thread
+    float acc[H2];
+#pragma unroll
+    for (int k = 0; k < H2; ++k) acc[k] = 0.f;
+    float den = 0.f;
+    for (int i = 0; i < P; ++i) {
+        const float2 ml = *reinterpret_cast<const float2 *>(p.ws_ml + ((slot0 + i) * BM + row) * 2);
+        const float wi = (M == -INFINITY || ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
+        den += wi * ml.y;
+        const float *o = p.ws_o + ((slot0 + i) * BM + row) * D + half * H2;
+#pragma unroll
+        for (int k = 0; k < H2; k += 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(o + k);
+            acc[k] += wi * v.x;
+            acc[k + 1] += wi * v.y;
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const int64_t rs = static_cast<int64_t>(p.num_heads) * D;
+    uint16_t *orow = p.out + (qa + q) * rs + head * D + half * H2;
+#pragma unroll
+    for (int k = 0; k < H2; k += 2)
+        *reinterpret_cast<uint32_t *>(orow + k) = pack2<T>(acc[k] * inv, acc[k + 1] * inv);
 }
 
 }  // namespace attn

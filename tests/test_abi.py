@@ -31,7 +31,8 @@ def lib():
 
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
-    assert set(names) >= {"attn_varlen_fwd", "attn_paged_decode", "attn_status_string",
+    assert set(names) >= {"attn_varlen_fwd", "attn_varlen_fwd_workspace_size",
+                          "attn_paged_decode", "attn_status_string",
                           "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
@@ -48,11 +49,13 @@ def test_status_strings(lib):
 
 def varlen(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=1, max_seqlen_q=16,
-             total_q=16, total_k=16, num_heads=2, head_dim=128, scale=0.1, dtype=0, out=FAKE)
+             total_q=16, total_k=16, num_heads=2, head_dim=128, scale=0.1, dtype=0, ws=None,
+             ws_bytes=0, out=FAKE)
     a.update(kw)
     return lib.attn_varlen_fwd(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["num_seqs"],
                                a["max_seqlen_q"], a["total_q"], a["total_k"], a["num_heads"],
-                               a["head_dim"], a["scale"], a["dtype"], a["out"], None)
+                               a["head_dim"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"],
+                               a["out"], None)
 
 
 def test_varlen_argument_errors(lib):
@@ -71,6 +74,7 @@ def test_varlen_argument_errors(lib):
     assert varlen(lib, k=None) == INVALID              # keys exist (total_k = 16)
     assert varlen(lib, k=FAKE + 8) == INVALID          # not 16-byte aligned
     assert varlen(lib, cu_q=FAKE + 2) == INVALID       # not 4-byte aligned
+    assert varlen(lib, ws=FAKE + 16, ws_bytes=1 << 20) == INVALID   # not 256-byte aligned
 
 
 def test_varlen_empty_work_is_ok_without_launch(lib):

@@ -142,3 +142,30 @@ def test_workload_s276_h4_d72_full():
                                   "prefill_s65556_h16_d72"])
 def test_workload_sampled_rows(name):
     sampled_check(name)
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_split_last_wave_matches_whole_items(D):
+    # 516 heads x 1 query tile: one full wave of workgroups plus a few items,
+    # which the library splits into key ranges (5 key tiles over up to 8
+    # ranges, so some ranges are empty) and merges
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    inp = gen.prefill_inputs([300], 516, D, seed=77)
+    assert attn_varlen_fwd_workspace_size(1, 300, 516, D) > 0
+    d = to_gpu(inp)
+    split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=300)
+    whole = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=300,
+                            workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 300, 64)
+    heads = np.concatenate([rng.integers(0, 516, 32), rng.integers(508, 516, 32)])
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
+    check(f64(split[idx]), ref, f"split D={D}", ref_abs=ref_abs)
+    check(f64(whole[idx]), ref, f"whole D={D}", ref_abs=ref_abs)
+    check(f64(split), f64(whole), f"split vs whole D={D}")
