@@ -436,12 +436,9 @@ void prefill_fwd_kernel(PrefillParams p)
         for (int i = 0; i < KD; ++i) kq[i] = kop(i);
         const f32x16 zero = {};
         uint32_t pw[16];
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int ks = i >> 1, kb2 = i & 1;
-            if (i + KD < NS) kq[(i + KD) % (KD + 1)] = kop(i + KD);
-            nxt[kb2] = T::mfma32(kq[i % (KD + 1)], qreg[ks], ks == 0 ? zero : nxt[kb2]);
-            const int pb = (16 * i) / NS, pe = (16 * (i + 1)) / NS;
+        // exponentials, 16-bit packing and row sums of value pairs [pb, pe)
+        // of tile t (pair pi = keys 2 (pi & 7), +1 of 32-key block pi >> 3)
+        auto exp_pairs = [&](int pb, int pe) {
 #pragma unroll
             for (int pi = pb; pi < pe; ++pi) {
                 const int kb = pi >> 3, r = 2 * (pi & 7);
@@ -460,12 +457,27 @@ void prefill_fwd_kernel(PrefillParams p)
                     }
                 }
             }
+        };
+        // The VALU work of a tile is spread over all its MFMAs: pairs
+        // 0 .. NA-1 ride along the NS S MFMAs, the last 16 - NA along the
+        // first PV MFMAs (before the MFMAs that use them), and the row max of
+        // the next tile along all PV MFMAs.
+        constexpr int NA = 10;
+        constexpr int NPV = 4 * S::DBLK;
+        constexpr int NB = 2 * S::DBLK;   // PV MFMAs carrying the late pairs
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int ks = i >> 1, kb2 = i & 1;
+            if (i + KD < NS) kq[(i + KD) % (KD + 1)] = kop(i + KD);
+            nxt[kb2] = T::mfma32(kq[i % (KD + 1)], qreg[ks], ks == 0 ? zero : nxt[kb2]);
+            exp_pairs((NA * i) / NS, (NA * (i + 1)) / NS);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (decltype(masked)::value) mask_tail(t + 1, nxt);
         float mx = -INFINITY;
         pv(par, pw, [&](int j) {
-            mx = max_part(nxt, j, 4 * S::DBLK, mx);
+            if (j < NB) exp_pairs(NA + ((16 - NA) * j) / NB, NA + ((16 - NA) * (j + 1)) / NB);
+            mx = max_part(nxt, j, NPV, mx);
             __builtin_amdgcn_sched_barrier(0);
         });
         max_finish(mx, t + 1 < t1);
