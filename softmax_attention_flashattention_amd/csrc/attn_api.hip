@@ -8,6 +8,7 @@
 #include "attn.h"
 #include "decode_kernel.hpp"
 #include "prefill_kernel.hpp"
+#include "prefill_wide_kernel.hpp"
 
 namespace {
 
@@ -17,15 +18,23 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// head_dim 128 runs the 64-rows-per-wave kernel, head_dim 72 the 32-row one.
+template <int D> constexpr int prefill_rows() { return D == 128 ? attn::kWideBM : attn::prefill_bm<D>(); }
+
 template <int D, typename T>
 int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
-                       dim3(attn::prefill_threads<D>()), 0, stream, p);
+    constexpr int BM = prefill_rows<D>();
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((attn::prefill_fwd_wide_kernel<T>), dim3(static_cast<unsigned>(grid)),
+                           dim3(attn::kWideThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
+                           dim3(attn::prefill_threads<D>()), 0, stream, p);
     int rc = launch_status();
     if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
-    hipLaunchKernelGGL((attn::prefill_merge_kernel<D, T>), dim3(static_cast<unsigned>(p.total_work - p.whole_work)),
-                       dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>), dim3(static_cast<unsigned>(p.total_work - p.whole_work)),
+                       dim3(2 * BM), 0, stream, p);
     return launch_status();
 }
 
@@ -37,10 +46,14 @@ int prefill_slots()
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>,
-                                                     attn::prefill_threads<D>(), 0) != hipSuccess)
-        return 0;
-    return cus * per_cu;
+    hipError_t e;
+    if constexpr (D == 128)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_wide_kernel<attn::Bf16>,
+                                                         attn::kWideThreads, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>,
+                                                         attn::prefill_threads<D>(), 0);
+    return e == hipSuccess ? cus * per_cu : 0;
 }
 
 // How the work items are launched.  When the last wave of workgroups would
@@ -137,7 +150,7 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, in
 {
     if (num_seqs <= 0 || max_seqlen_q <= 0 || num_heads <= 0) return 0;
     if (head_dim != 72 && head_dim != 128) return 0;
-    const int bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
+    const int bm = head_dim == 128 ? prefill_rows<128>() : prefill_rows<72>();
     const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
     const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
@@ -163,7 +176,7 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
         !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
         return ATTN_ERR_INVALID_ARG;
 
-    const int bm = head_dim == 128 ? attn::prefill_bm<128>() : attn::prefill_bm<72>();
+    const int bm = head_dim == 128 ? prefill_rows<128>() : prefill_rows<72>();
     const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
     if (work > INT32_MAX / 8) return ATTN_ERR_INVALID_ARG;

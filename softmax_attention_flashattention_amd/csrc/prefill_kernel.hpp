@@ -547,12 +547,11 @@ void prefill_fwd_kernel(PrefillParams p)
 }
 
 // Log-sum-exp merge of the key ranges of the split work items: one
-// workgroup per item, two threads per query row (each half of head_dim).
-template <int D, typename T>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p)
+// workgroup per item of BM query rows, two threads per row (each half of
+// head_dim).
+template <int D, int BM, typename T>
+__global__ __launch_bounds__(2 * BM) void prefill_merge_kernel(PrefillParams p)
 {
-    constexpr int BM = prefill_bm<D>();
-    static_assert(2 * BM == 256, "two threads per query row");
     const int w = p.whole_work + blockIdx.x;
     if (w >= p.total_work) return;
     const int qtile = w % p.num_qtiles;
