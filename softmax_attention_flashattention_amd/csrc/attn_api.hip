@@ -18,14 +18,17 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// head_dim 128 runs the 64-rows-per-wave kernel, head_dim 72 the 32-row one.
-template <int D> constexpr int prefill_rows() { return D == 128 ? attn::kWideBM : attn::prefill_bm<D>(); }
+// Which prefill kernel runs: the 64-rows-per-wave one (head_dim 128 only) or
+// the 32-row one.  The 32-row kernel is currently the faster of the two.
+constexpr bool kUseWide = false;
+template <int D> constexpr bool use_wide() { return kUseWide && D == 128; }
+template <int D> constexpr int prefill_rows() { return use_wide<D>() ? attn::kWideBM : attn::prefill_bm<D>(); }
 
 template <int D, typename T>
 int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
 {
     constexpr int BM = prefill_rows<D>();
-    if constexpr (D == 128)
+    if constexpr (use_wide<D>())
         hipLaunchKernelGGL((attn::prefill_fwd_wide_kernel<T>), dim3(static_cast<unsigned>(grid)),
                            dim3(attn::kWideThreads), 0, stream, p);
     else
@@ -47,7 +50,7 @@ int prefill_slots()
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     hipError_t e;
-    if constexpr (D == 128)
+    if constexpr (use_wide<D>())
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_wide_kernel<attn::Bf16>,
                                                          attn::kWideThreads, 0);
     else
