@@ -8,7 +8,6 @@
 #include "attn.h"
 #include "decode_kernel.hpp"
 #include "prefill_kernel.hpp"
-#include "prefill_wide_kernel.hpp"
 
 namespace {
 
@@ -18,22 +17,14 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// Which prefill kernel runs: the 64-rows-per-wave one (head_dim 128 only) or
-// the 32-row one.  The 32-row kernel is currently the faster of the two.
-constexpr bool kUseWide = false;
-template <int D> constexpr bool use_wide() { return kUseWide && D == 128; }
-template <int D> constexpr int prefill_rows() { return use_wide<D>() ? attn::kWideBM : attn::prefill_bm<D>(); }
+template <int D> constexpr int prefill_rows() { return attn::prefill_bm<D>(); }
 
 template <int D, typename T>
 int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
 {
     constexpr int BM = prefill_rows<D>();
-    if constexpr (use_wide<D>())
-        hipLaunchKernelGGL((attn::prefill_fwd_wide_kernel<T>), dim3(static_cast<unsigned>(grid)),
-                           dim3(attn::kWideThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
-                           dim3(attn::prefill_threads<D>()), 0, stream, p);
+    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::prefill_threads<D>()), 0, stream, p);
     int rc = launch_status();
     if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
     hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>), dim3(static_cast<unsigned>(p.total_work - p.whole_work)),
@@ -49,13 +40,8 @@ int prefill_slots()
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    hipError_t e;
-    if constexpr (use_wide<D>())
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_wide_kernel<attn::Bf16>,
-                                                         attn::kWideThreads, 0);
-    else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>,
-                                                         attn::prefill_threads<D>(), 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>, attn::prefill_threads<D>(), 0);
     return e == hipSuccess ? cus * per_cu : 0;
 }
 

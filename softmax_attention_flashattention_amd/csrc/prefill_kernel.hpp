@@ -266,6 +266,16 @@ void prefill_fwd_kernel(PrefillParams p)
                 if (active(i)) vst[i] = buf_ld16(r, voff[i]);
         }
     };
+    // one DMA instruction (rows RW w + 4 j .. +3) of a K or V tile
+    auto dma_k = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
+    };
+    auto dma_v = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
+            static_cast<int>(4 * j * row_bytes), 0, 0);
+    };
     auto store_k = [&](auto par) {
         if constexpr (!DIRECT) {
 #pragma unroll
@@ -417,8 +427,23 @@ void prefill_fwd_kernel(PrefillParams p)
     // masked: whether S(t+1) may be the partial last tile (a branch; kept out
     // of the main loop so that the exponentials are not moved past it)
     auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2], auto masked) {
-        load_k(t + 2, par);
-        load_v(t + 1, npar);
+        // K(t+2) goes to the buffer K(t) left, V(t+1) to the one V(t-1) left.
+        // Direct DMA: one instruction after every other S MFMA (the 2 DJ
+        // instructions issued in one burst stall the wave at issue).
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_head + static_cast<int64_t>(t + 2) * BN * rs, tile_bytes(t + 2));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_head + static_cast<int64_t>(t + 1) * BN * rs, tile_bytes(t + 1));
+        if constexpr (!DIRECT) {
+            load_k(t + 2, par);
+            load_v(t + 1, npar);
+        }
+        auto dma_slot = [&](int mfma) {
+            if constexpr (DIRECT) {
+                if (mfma % 2 == 0 && mfma / 2 < 2 * DJ) {
+                    const int n = mfma / 2;
+                    if (n < DJ) dma_k(rk, par, n); else dma_v(rv, npar, n - DJ);
+                }
+            }
+        };
         __builtin_amdgcn_sched_barrier(0);
 
         // The NS MFMAs of S(t+1) = K(t+1) Q^T, in the order ks outer, kb2
@@ -470,6 +495,7 @@ void prefill_fwd_kernel(PrefillParams p)
             const int ks = i >> 1, kb2 = i & 1;
             if (i + KD < NS) kq[(i + KD) % (KD + 1)] = kop(i + KD);
             nxt[kb2] = T::mfma32(kq[i % (KD + 1)], qreg[ks], ks == 0 ? zero : nxt[kb2]);
+            dma_slot(i);
             exp_pairs((NA * i) / NS, (NA * (i + 1)) / NS);
             __builtin_amdgcn_sched_barrier(0);
         }
