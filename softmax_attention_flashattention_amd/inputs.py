@@ -14,10 +14,19 @@ element size), V cache ``[num_blocks, kv_heads, head_size, block_size]``,
 identity-ordered block table ``bt[i][j] = i * max_blocks_per_seq + j`` and
 every ``seq_lens`` entry equal to ``ctx_len``.
 
+For the chunked delta-rule output ("chunk_delta_rule_output" #004, Input
+Generation): q ~ 0.02 N(0, 1) ``[batch, tokens, q_heads, key_dim]``, k ~ N(0, 1)
+of q's shape (the page draws it with randn_like, unscaled), v ~ 0.02 N(0, 1)
+``[batch, tokens, heads, value_dim]``, h ~ 0.02 N(0, 1) ``[batch, chunks,
+heads, key_dim, value_dim]`` and float32 g = -U[0, 1) ``[batch, tokens,
+heads]``.
+
 The pages draw without a seed on the device; here every tensor is drawn on the
 CPU from ``torch.Generator().manual_seed(seed)`` in float32, in the pages'
-order (q, k, v; query, k_cache, v_cache) and rounded to the 16-bit type with
-round-to-nearest-even, so the oracle and the GPU see the same bits.
+order (q, k, v; query, k_cache, v_cache; q, k, v, h, g) and rounded to the
+16-bit type with round-to-nearest-even (a scaled draw is rounded, scaled in
+float32 and rounded again, as the page's 16-bit multiply does), so the oracle
+and the GPU see the same bits.
 """
 import torch
 
@@ -39,6 +48,15 @@ WORKLOADS = {
                                             seed=1004),
     "prefill_s65556_h16_d72": dict(kind="prefill", seq_lens=[65556], num_heads=16, head_dim=72,
                                    seed=1005),
+}
+
+# Chunked delta-rule output workloads: rows 15, 13, 8 and 0 of the
+# "chunk_delta_rule_output" Shapes table (chunk 64, key_dim = value_dim = 128).
+CHUNK_WORKLOADS = {
+    "chunk_t14807_h32_hq16": dict(batch=1, tokens=14807, num_q_heads=16, num_heads=32, seed=1006),
+    "chunk_t4195_h32_hq16": dict(batch=1, tokens=4195, num_q_heads=16, num_heads=32, seed=1007),
+    "chunk_t704_h16_hq8": dict(batch=1, tokens=704, num_q_heads=8, num_heads=16, seed=1008),
+    "chunk_t64_h32_hq16": dict(batch=1, tokens=64, num_q_heads=16, num_heads=32, seed=1009),
 }
 
 
@@ -115,8 +133,28 @@ def permute_blocks(inputs, seed):
     return out
 
 
+def chunk_inputs(batch, tokens, num_q_heads, num_heads, seed, key_dim=128, value_dim=128,
+                 chunk_size=64, dtype="bf16"):
+    """q, k, v, h (16-bit) and g (float32) of the chunked delta-rule output, on the CPU."""
+    gen = torch.Generator().manual_seed(int(seed))
+    dt = _DT[dtype]
+    nc = (tokens + chunk_size - 1) // chunk_size
+
+    def scaled(shape):
+        return (_randn(gen, shape, dtype).float() * 0.02).to(dt)
+
+    q = scaled((batch, tokens, num_q_heads, key_dim))
+    k = _randn(gen, (batch, tokens, num_q_heads, key_dim), dtype)
+    v = scaled((batch, tokens, num_heads, value_dim))
+    h = scaled((batch, nc, num_heads, key_dim, value_dim))
+    g = -torch.rand(batch, tokens, num_heads, generator=gen, dtype=torch.float32)
+    return {"q": q, "k": k, "v": v, "h": h, "g": g, "chunk_size": chunk_size}
+
+
 def workload_inputs(name):
-    """Inputs of one named workload from ``WORKLOADS``."""
+    """Inputs of one named workload from ``WORKLOADS`` or ``CHUNK_WORKLOADS``."""
+    if name in CHUNK_WORKLOADS:
+        return chunk_inputs(**CHUNK_WORKLOADS[name])
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
     if kind == "prefill":

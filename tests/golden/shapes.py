@@ -35,3 +35,7 @@ def prefill_rows():
 
 def decode_rows():
     return _read("paged_attention_decode_shapes.tsv")
+
+
+def chunk_rows():
+    return _read("chunk_delta_rule_output_shapes.tsv")
