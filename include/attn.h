@@ -1,6 +1,6 @@
 /*
  * attn.h -- libattn: exact softmax attention forward on AMD Instinct MI355X
- * (gfx950, CDNA4).
+ * (gfx950, CDNA4), and the output step of chunked linear attention.
  *
  * Two operators share one definition: for every sequence and head,
  *
@@ -9,7 +9,9 @@
  * accumulated in fp32 and written in the input's 16-bit type (bf16 or fp16).
  * The definition and both data layouts are those of the atrex-bench operator
  * pages "attention_forward" (#001) and "paged_attention_decode" (#024),
- * sections "Reference Implementation" and "Input Generation".
+ * sections "Reference Implementation" and "Input Generation".  A third entry
+ * point, attn_chunk_delta_out, computes the page "chunk_delta_rule_output"
+ * (#004): a gated, causal, unnormalised variant over chunks of 64 tokens.
  *
  * Conventions shared by every entry point
  *  - Every tensor pointer is device memory owned by the caller.  The library
@@ -156,6 +158,37 @@ int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t blo
 size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads,
                                         int32_t head_size, int32_t max_blocks_per_seq,
                                         int32_t block_size, int32_t partition_size);
+
+/*
+ * attn_chunk_delta_out -- output step of chunked gated delta-rule linear
+ * attention.
+ *
+ * Defined by "chunk_delta_rule_output" (#004), Reference Implementation and
+ * Input Generation.  For every batch b, value head hd and chunk c of
+ * chunk_size consecutive tokens (the last chunk may be short), with query
+ * head hq = min(hd / max(num_heads / num_q_heads, 1), num_q_heads - 1) and
+ * token rows i, j of the chunk:
+ *   a[i][j] = <q_i, k_j> exp(g_i - g_j) if j <= i and g_i <= g_j, else 0,
+ *             rounded to the 16-bit type (to nearest, ties to even)
+ *   out_i   = scale (exp(g_i) q_i h_c + sum_j a[i][j] v_j)
+ * accumulated in fp32.  Unlike the softmax entries there is no normalisation.
+ *
+ *  q, k      [batch, tokens, num_q_heads, key_dim], dtype
+ *  v         [batch, tokens, num_heads, value_dim], dtype
+ *  h         [batch, ceil(tokens / chunk_size), num_heads, key_dim, value_dim],
+ *            dtype: the state each chunk starts from
+ *  g         [batch, tokens, num_heads] float32 (log gates), 4-byte aligned
+ *  key_dim, value_dim  128; chunk_size 64 (others: ATTN_ERR_UNSUPPORTED)
+ *  scale     finite; the page uses key_dim^-1/2
+ *  out       [batch, tokens, num_heads, value_dim], dtype; every row written
+ *
+ * batch == 0 or tokens == 0 is a valid no-op (pointers may then be NULL).
+ */
+int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h,
+                         const float *g, int32_t batch, int32_t tokens, int32_t num_q_heads,
+                         int32_t num_heads, int32_t key_dim, int32_t value_dim,
+                         int32_t chunk_size, float scale, int32_t dtype, void *out,
+                         void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *attn_status_string(int32_t status);

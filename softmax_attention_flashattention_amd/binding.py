@@ -59,6 +59,9 @@ def _load():
     lib.attn_paged_decode_num_partitions.restype = i32
     lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_paged_decode_workspace_size.restype = sz
+    lib.attn_chunk_delta_out.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                         P, P]
+    lib.attn_chunk_delta_out.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -209,4 +212,42 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
                                    ws_len, _ptr(out), _stream(query.device))
     if rc != 0:
         raise AttnError("attn_paged_decode", rc)
+    return out
+
+
+def attn_chunk_delta_out(q, k, v, h, g, chunk_size=64, scale=None, out=None):
+    """Output step of chunked gated delta-rule linear attention (calls
+    ``attn_chunk_delta_out``).
+
+    q, k [B, T, Hq, K] and v [B, T, H, V] in bf16 or fp16; h [B, ceil(T /
+    chunk_size), H, K, V] in the same dtype; g [B, T, H] float32.  Shapes are
+    derived as the operator page does (``batch, tokens, num_q_heads, key_dim
+    = q.shape``, ``num_heads, value_dim = v.shape[2], v.shape[3]``).
+    ``scale`` defaults to K**-0.5.  Returns out [B, T, H, V] in v's dtype.
+    """
+    fp16 = (torch.bfloat16, torch.float16)
+    _need(q, "q", fp16, 4)
+    _need(k, "k", q.dtype, 4)
+    _need(v, "v", q.dtype, 4)
+    _need(h, "h", q.dtype, 5)
+    _need(g, "g", torch.float32, 3)
+    B, T, Hq, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    nc = (T + chunk_size - 1) // chunk_size
+    if tuple(k.shape) != (B, T, Hq, K) or tuple(v.shape[:2]) != (B, T):
+        raise ValueError("q, k must be [B, T, Hq, K] and v [B, T, H, V]")
+    if tuple(h.shape) != (B, nc, H, K, V) or tuple(g.shape) != (B, T, H):
+        raise ValueError("h must be [B, ceil(T / chunk_size), H, K, V] and g [B, T, H]")
+    scale = float(K) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(v)
+    else:
+        _need(out, "out", v.dtype, 4)
+        if out.shape != v.shape:
+            raise ValueError("out must have v's shape")
+    rc = _load().attn_chunk_delta_out(_ptr(q), _ptr(k), _ptr(v), _ptr(h), _ptr(g), B, T, Hq, H, K,
+                                      V, int(chunk_size), scale, _DTYPE[q.dtype], _ptr(out),
+                                      _stream(q.device))
+    if rc != 0:
+        raise AttnError("attn_chunk_delta_out", rc)
     return out

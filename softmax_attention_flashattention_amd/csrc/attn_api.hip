@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "attn.h"
+#include "chunk_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "prefill_kernel.hpp"
 
@@ -281,6 +282,53 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, head_size, grid, s)
                                     : dispatch_decode<attn::Fp16>(p, head_size, grid, s);
+}
+
+int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h, const float *g,
+                         int32_t batch, int32_t tokens, int32_t num_q_heads, int32_t num_heads,
+                         int32_t key_dim, int32_t value_dim, int32_t chunk_size, float scale,
+                         int32_t dtype, void *out, void *stream)
+{
+    if (batch < 0 || tokens < 0 || num_q_heads <= 0 || num_heads <= 0 || key_dim <= 0 ||
+        value_dim <= 0 || chunk_size <= 0)
+        return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (key_dim != attn::kChunkDim || value_dim != attn::kChunkDim || chunk_size != attn::kChunk)
+        return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || tokens == 0) return ATTN_OK;
+    if (!q || !k || !v || !h || !g || !out) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(h, 16) || !aligned(out, 16) ||
+        !aligned(g, 4))
+        return ATTN_ERR_INVALID_ARG;
+    const int64_t num_chunks = (static_cast<int64_t>(tokens) + chunk_size - 1) / chunk_size;
+    const int64_t grid = static_cast<int64_t>(batch) * num_chunks * num_heads;
+    // the kernel's buffer offsets are 32-bit: one chunk of v rows must span < 4 GiB
+    const int64_t v_span = static_cast<int64_t>(chunk_size) * num_heads * value_dim * 2;
+    if (grid > INT32_MAX || v_span > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+
+    attn::ChunkParams p;
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.h = static_cast<const uint16_t *>(h);
+    p.g = g;
+    p.out = static_cast<uint16_t *>(out);
+    p.batch = batch;
+    p.tokens = tokens;
+    p.num_q_heads = num_q_heads;
+    p.num_heads = num_heads;
+    p.num_chunks = static_cast<int>(num_chunks);
+    p.per_q = num_heads / num_q_heads > 1 ? num_heads / num_q_heads : 1;
+    p.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ATTN_DTYPE_BF16)
+        hipLaunchKernelGGL((attn::chunk_delta_out_kernel<attn::Bf16>), dim3(static_cast<unsigned>(grid)),
+                           dim3(attn::kChunkThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn::chunk_delta_out_kernel<attn::Fp16>), dim3(static_cast<unsigned>(grid)),
+                           dim3(attn::kChunkThreads), 0, s, p);
+    return launch_status();
 }
 
 }  // extern "C"

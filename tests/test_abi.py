@@ -33,7 +33,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"attn_varlen_fwd", "attn_varlen_fwd_workspace_size",
                           "attn_paged_decode", "attn_status_string",
-                          "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions"}
+                          "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions",
+                          "attn_chunk_delta_out"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
 
@@ -128,6 +129,37 @@ def test_decode_workspace_rules(lib):
 
 def test_decode_empty_batch_is_ok_without_launch(lib):
     assert decode(lib, num_seqs=0, query=None) == OK
+
+
+def chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, h=FAKE, g=FAKE, batch=1, tokens=100, hq=16, hv=32, kd=128,
+             vd=128, cs=64, scale=0.1, dtype=0, out=FAKE)
+    a.update(kw)
+    return lib.attn_chunk_delta_out(a["q"], a["k"], a["v"], a["h"], a["g"], a["batch"], a["tokens"],
+                                    a["hq"], a["hv"], a["kd"], a["vd"], a["cs"], a["scale"],
+                                    a["dtype"], a["out"], None)
+
+
+def test_chunk_argument_errors(lib):
+    assert chunk(lib, kd=64) == UNSUPPORTED
+    assert chunk(lib, vd=256) == UNSUPPORTED
+    assert chunk(lib, cs=32) == UNSUPPORTED
+    assert chunk(lib, batch=-1) == INVALID
+    assert chunk(lib, tokens=-5) == INVALID
+    assert chunk(lib, hq=0) == INVALID
+    assert chunk(lib, hv=0) == INVALID
+    assert chunk(lib, cs=0) == INVALID
+    assert chunk(lib, dtype=3) == INVALID
+    assert chunk(lib, scale=float("inf")) == INVALID
+    assert chunk(lib, h=None) == INVALID
+    assert chunk(lib, g=None) == INVALID
+    assert chunk(lib, out=FAKE + 8) == INVALID         # not 16-byte aligned
+    assert chunk(lib, g=FAKE + 2) == INVALID           # not 4-byte aligned
+
+
+def test_chunk_empty_input_is_ok_without_launch(lib):
+    assert chunk(lib, tokens=0, q=None, k=None, v=None, h=None, g=None, out=None) == OK
+    assert chunk(lib, batch=0, q=None) == OK
 
 
 def test_binding_names_match_the_header():
