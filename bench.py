@@ -34,7 +34,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PREFILL = "prefill_s16742_h32_d128"
 DECODE = "decode_b256_ctx64_h16_kv16_d128"
-KERNEL_SOURCES = ["prefill_kernel.hpp", "decode_kernel.hpp", "device_common.hpp"]
+CHUNK = "chunk_t14807_h32_hq16"
+# the sources each kernel's counter figures depend on
+KERNEL_SOURCES = {
+    "prefill_fwd_kernel": ["prefill_kernel.hpp", "device_common.hpp"],
+    "decode_partition_kernel": ["decode_kernel.hpp", "device_common.hpp"],
+    "chunk_delta_out_kernel": ["chunk_kernel.hpp", "device_common.hpp"],
+}
+ALL_SOURCES = ["prefill_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp", "device_common.hpp"]
 
 
 def kernel_source_hash(names):
@@ -75,6 +82,13 @@ def decode_bytes(inp):
     tokens = int(inp["seq_lens"].clamp(min=0).sum())
     return (2 * tokens * Hkv * D * el + 2 * S * Hq * D * el
             + inp["block_tables"].numel() * 4 + inp["seq_lens"].numel() * 4)
+
+
+def chunk_bytes(inp):
+    """Algorithmic bytes of one chunked delta-rule output call: q, k, v, h
+    and g read once, the output written once."""
+    return sum(inp[n].numel() * inp[n].element_size() for n in ("q", "k", "v", "h", "g")) \
+        + inp["v"].numel() * inp["v"].element_size()
 
 
 def cpu_baseline(budget_s):
@@ -158,15 +172,15 @@ def summarize_counters(pmc_dir):
                      "(KiB -> bytes); scales from a plain 1 GiB device copy"),
            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
            "copy_kernel": copy_kernel}
-    src_hash = kernel_source_hash(KERNEL_SOURCES)
-    for prefix in ("prefill_fwd_kernel", "decode_partition_kernel"):
+    for prefix in KERNEL_SOURCES:
         names = [k for k in fetch if prefix in k]
         if not names:
             continue
         k = names[0]
         rd = fetch[k] * fetch_scale * 1024.0
         wr = write.get(k, 0.0) * write_scale * 1024.0
-        out[prefix] = {"kernel": k, "source_hash": src_hash, "read_bytes": round(rd),
+        out[prefix] = {"kernel": k, "source_hash": kernel_source_hash(KERNEL_SOURCES[prefix]),
+                       "read_bytes": round(rd),
                        "write_bytes": round(wr), "bytes_per_launch": round(rd + wr)}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as f:
@@ -184,7 +198,7 @@ def main():
                     help="decode input copies cycled through (8 x 138 MB > 256 MB cache)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU work for the oracle baseline (0 skips it)")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "chunk", "copy"], default=None,
                     help="time one part alone (for profiling); 'copy' times a plain 1 GiB "
                          "device-to-device copy, the reference for HBM counter scaling")
     ap.add_argument("--prefill-workload", default=PREFILL,
@@ -203,7 +217,8 @@ def main():
         sys.exit(2)
 
     import torch
-    from softmax_attention_flashattention_amd import attn_paged_decode, attn_varlen_fwd
+    from softmax_attention_flashattention_amd import (attn_chunk_delta_out, attn_paged_decode,
+                                                      attn_varlen_fwd)
     from softmax_attention_flashattention_amd import inputs as gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -239,8 +254,18 @@ def main():
         attn_paged_decode(c["query"], c["k_cache"], c["v_cache"], c["block_tables"],
                           c["seq_lens"], out=d_out[i % len(d_copies)])
 
+    c_host = gen.workload_inputs(CHUNK)
+    ck = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in c_host.items()}
+    c_out = torch.empty_like(ck["v"])
+    cbytes = chunk_bytes(c_host)
+
+    def chunk_call():
+        attn_chunk_delta_out(ck["q"], ck["k"], ck["v"], ck["h"], ck["g"],
+                             chunk_size=ck["chunk_size"], out=c_out)
+
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
+    do_chunk = args.only in (None, "chunk")
     for i in range(args.warmup):
         if do_prefill:
             prefill_call()
@@ -284,12 +309,32 @@ def main():
         b.record()
         torch.cuda.synchronize()
         dec_avg = a.elapsed_time(b) / reps
+    # The chunked delta-rule output (a further operator, not part of the
+    # step): its own back-to-back launches.  One call streams 608 MB, beyond
+    # the 256 MB Infinity Cache, so no input rotation is needed.
+    chunk_avg = 0.0
+    if do_chunk:
+        for _ in range(args.warmup):
+            chunk_call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            chunk_call()
+        b.record()
+        torch.cuda.synchronize()
+        chunk_avg = a.elapsed_time(b) / args.steps
     tflops = flops / (pre_avg * 1e-3) / 1e12 if do_prefill else 0.0
     gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_decode else 0.0
 
-    src_hash = kernel_source_hash(KERNEL_SOURCES)
-    pre_traffic = profiled_traffic("prefill_fwd_kernel", src_hash) if p_name == PREFILL else None
-    dec_traffic = profiled_traffic("decode_partition_kernel", src_hash)
+    def traffic(prefix):
+        return profiled_traffic(prefix, kernel_source_hash(KERNEL_SOURCES[prefix]))
+
+    src_hash = kernel_source_hash(ALL_SOURCES)
+    pre_traffic = traffic("prefill_fwd_kernel") if p_name == PREFILL else None
+    dec_traffic = traffic("decode_partition_kernel")
+    chunk_traffic = traffic("chunk_delta_out_kernel")
+    cgbs = cbytes / (chunk_avg * 1e-3) / 1e9 if do_chunk else 0.0
 
     result = {
         "metric": "prefill attn TFLOP/s & % MFMA peak; paged-decode GB/s & % HBM peak",
@@ -331,6 +376,15 @@ def main():
                 "bytes_per_launch": dbytes, "avg_launch_us": round(dec_avg * 1e3, 3),
                 "avg_in_step_us": round(dec_step_avg * 1e3, 3),
                 "min_in_step_us": round(dec_ms[0] * 1e3, 3),
+            },
+        },
+        "chunk": {
+            "workload": CHUNK, "value": round(cgbs, 1), "unit": "GB/s",
+            "roofline": {
+                "bound": "hbm", "achieved": round(cgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(cgbs / PEAK_HBM_GBS, 4), "traffic": chunk_traffic,
+                "kernel": "chunk_delta_out_kernel<bf16>", "bytes_per_launch": cbytes,
+                "avg_launch_us": round(chunk_avg * 1e3, 3),
             },
         },
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
