@@ -189,6 +189,75 @@ def summarize_counters(pmc_dir):
     print(json.dumps(out, indent=1))
 
 
+def shapes_rows(torch, dev, which):
+    """Times every row of one operator page's Shapes table (seeded inputs of
+    the row's sizes) and prints one JSON line per row: the per-launch time
+    of back-to-back launches, the achieved rate against its roofline and the
+    page's production time for context."""
+    sys.path.insert(0, os.path.join(ROOT, "tests", "golden"))
+    import shapes
+    from softmax_attention_flashattention_amd import (attn_chunk_delta_out, attn_paged_decode,
+                                                      attn_varlen_fwd, attn_varlen_fwd_workspace_size)
+    from softmax_attention_flashattention_amd import inputs as gen
+
+    def timed(call, min_ms=30.0):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        n = 1
+        while True:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            if ms >= min_ms or n >= 4096:
+                return ms / n
+            n *= 4
+
+    rows = {"prefill": shapes.prefill_rows, "decode": shapes.decode_rows,
+            "chunk": shapes.chunk_rows}[which]()
+    for r in rows:
+        if which == "prefill":
+            x = gen.prefill_inputs([r["seq_len"]], r["num_heads"], r["head_dim"], seed=2000 + r["row"])
+            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+            out = torch.empty_like(d["q"])
+            ws = torch.empty(attn_varlen_fwd_workspace_size(1, x["max_seqlen_q"], r["num_heads"],
+                                                            r["head_dim"]), dtype=torch.uint8,
+                             device=dev)
+            ms = timed(lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"],
+                                               d["cu_seqlens_k"], max_seqlen_q=x["max_seqlen_q"],
+                                               out=out, workspace=ws))
+            work = prefill_flops(x)
+            rate, unit, peak = work / (ms * 1e-3) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+        elif which == "decode":
+            x = gen.decode_inputs(r["num_seqs"], r["ctx_len"], r["num_query_heads"],
+                                  r["num_kv_heads"], r["head_size"], seed=3000 + r["row"],
+                                  dtype=r["dtype"])
+            d = {k: v.to(dev) for k, v in x.items()}
+            out = torch.empty_like(d["query"])
+            ms = timed(lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"],
+                                                 d["block_tables"], d["seq_lens"], out=out))
+            work = decode_bytes(x)
+            rate, unit, peak = work / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+        else:
+            x = gen.chunk_inputs(r["batch_size"], r["token_count"], r["num_q_heads"],
+                                 r["num_v_heads"], seed=4000 + r["row"])
+            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+            out = torch.empty_like(d["v"])
+            ms = timed(lambda: attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"], out=out))
+            work = chunk_bytes(x)
+            rate, unit, peak = work / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+        sizes = {k: v for k, v in r.items() if k not in ("t_sol_us", "t_prod_us")}
+        print(json.dumps({"shapes": which, **sizes, "us_per_launch": round(ms * 1e3, 2),
+                          "achieved": round(rate, 1), "unit": unit,
+                          "frac": round(rate / peak, 4), "page_t_prod_us": r["t_prod_us"]}),
+              flush=True)
+        del x, d, out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +274,9 @@ def main():
                     choices=[k for k in ("prefill_s276_h4_d72", "prefill_s8136_h16_d72",
                                          "prefill_s16742_h32_d128", "prefill_s65556_h16_d72")],
                     help="prefill workload of the step (default: the head_dim-128 roofline case)")
+    ap.add_argument("--shapes", choices=["prefill", "decode", "chunk"], default=None,
+                    help="time every row of that operator page's Shapes table (one JSON line "
+                         "per row) and exit")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
                          "(no GPU needed)")
@@ -226,6 +298,8 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.only == "copy":
         return copy_reference(torch, dev, args)
+    if args.shapes:
+        return shapes_rows(torch, dev, args.shapes)
 
     p_name = args.prefill_workload
     p_host = gen.workload_inputs(p_name)
