@@ -77,9 +77,10 @@ typedef enum attn_dtype {
  *                 attn_varlen_fwd_workspace_size(...) bytes.  When the work
  *                 items would leave the device's last wave of workgroups at
  *                 most half full, those items are split into key ranges
- *                 whose partial results go here and a second kernel merges
- *                 them.  NULL (or too small) runs every item whole: the same
- *                 result, only slower in that case.
+ *                 (when there are fewer items than half the device holds at
+ *                 once, every item is) whose partial results go here and a
+ *                 second kernel merges them.  NULL (or too small) runs every
+ *                 item whole: the same result, only slower in that case.
  *  out            [total_q, num_heads, head_dim], dtype.  Only rows inside a
  *                 query segment are written; a sequence with query rows but
  *                 no key rows gets all-zero rows.  Other rows are untouched.

@@ -28,8 +28,9 @@ int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t strea
                        dim3(attn::prefill_threads<D>()), 0, stream, p);
     int rc = launch_status();
     if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
-    hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>), dim3(static_cast<unsigned>(p.total_work - p.whole_work)),
-                       dim3(2 * BM), 0, stream, p);
+    hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>),
+                       dim3(static_cast<unsigned>((p.total_work - p.whole_work) * attn::merge_blocks<D, BM>())),
+                       dim3(attn::kMergeThreads), 0, stream, p);
     return launch_status();
 }
 
@@ -54,7 +55,7 @@ struct PrefillPlan {
     size_t ws_o_bytes = 0, ws_bytes = 0;
 };
 
-PrefillPlan plan_prefill(int64_t work, int slots, int bm, int head_dim)
+PrefillPlan plan_prefill(int64_t work, int slots, int bm, int head_dim, int64_t key_tiles)
 {
     PrefillPlan pl;
     pl.work = work;
@@ -63,6 +64,17 @@ PrefillPlan plan_prefill(int64_t work, int slots, int bm, int head_dim)
     if (full >= 1 && rest > 0 && 2 * rest <= slots) {
         pl.parts = slots / rest < 8 ? slots / rest : 8;
         pl.whole = (full * slots) / 8 * 8;
+    } else if (full == 0 && work > 0 && 2 * work <= slots) {
+        // fewer items than half the device holds: split every item into
+        // ranges of at least four key tiles, when there are 16 or more
+        // (key_tiles estimates the keys per sequence from the query length;
+        // below that the merge costs more than the split gains)
+        int64_t parts = slots / work < 8 ? slots / work : 8;
+        if (parts > key_tiles / 4) parts = key_tiles / 4;
+        if (key_tiles >= 16 && parts >= 2) {
+            pl.parts = parts;
+            pl.whole = 0;
+        }
     }
     if (pl.parts < 2) {
         pl.parts = 1;
@@ -144,7 +156,8 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, in
     const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
     const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
-    return plan_prefill(work, slots, bm, head_dim).ws_bytes;
+    const int64_t key_tiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBN - 1) / attn::kPrefillBN;
+    return plan_prefill(work, slots, bm, head_dim, key_tiles).ws_bytes;
 }
 
 int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
@@ -171,9 +184,10 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
     if (work > INT32_MAX / 8) return ATTN_ERR_INVALID_ARG;
     const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
-    PrefillPlan pl = plan_prefill(work, slots, bm, head_dim);
+    const int64_t key_tiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBN - 1) / attn::kPrefillBN;
+    PrefillPlan pl = plan_prefill(work, slots, bm, head_dim, key_tiles);
     if (pl.parts > 1 && (!workspace || workspace_bytes < pl.ws_bytes))
-        pl = plan_prefill(work, 0, bm, head_dim);    // no room for the split: run items whole
+        pl = plan_prefill(work, 0, bm, head_dim, key_tiles);    // no room for the split: run items whole
 
     attn::PrefillParams p;
     p.q = static_cast<const uint16_t *>(q);

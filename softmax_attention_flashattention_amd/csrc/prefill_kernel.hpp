@@ -572,13 +572,24 @@ void prefill_fwd_kernel(PrefillParams p)
     }
 }
 
-// Log-sum-exp merge of the key ranges of the split work items: one
-// workgroup per item of BM query rows, two threads per row (each half of
-// head_dim).
+// Log-sum-exp merge of the key ranges of the split work items.  Each thread
+// owns four consecutive output values of one row of one item and walks the
+// item's ranges; consecutive threads own consecutive values, so every
+// partial-row load is contiguous across the wave.  kMergeBlocks<D, BM>
+// workgroups of kMergeThreads per item.
+constexpr int kMergeThreads = 256;
+template <int D, int BM> constexpr int merge_blocks() { return (BM * (D / 4) + kMergeThreads - 1) / kMergeThreads; }
+
 template <int D, int BM, typename T>
-__global__ __launch_bounds__(2 * BM) void prefill_merge_kernel(PrefillParams p)
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillParams p)
 {
-    const int w = p.whole_work + blockIdx.x;
+    constexpr int C4 = D / 4;   // float4 columns per row
+    constexpr int NB = merge_blocks<D, BM>();
+    const int item = blockIdx.x / NB;
+    const int e = (blockIdx.x % NB) * kMergeThreads + threadIdx.x;
+    if (e >= BM * C4) return;
+    const int row = e / C4, c4 = e % C4;
+    const int w = p.whole_work + item;
     if (w >= p.total_work) return;
     const int qtile = w % p.num_qtiles;
     const int sh = w / p.num_qtiles;
@@ -588,37 +599,29 @@ __global__ __launch_bounds__(2 * BM) void prefill_merge_kernel(PrefillParams p)
     qa = qa < 0 ? 0 : (qa > p.total_q ? p.total_q : qa);
     qb = qb < qa ? qa : (qb > p.total_q ? p.total_q : qb);
     const int Sq = static_cast<int>(qb - qa);
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
     const int q = qtile * BM + row;
     if (q >= Sq) return;
     const int P = p.split_parts;
-    const int64_t slot0 = static_cast<int64_t>(blockIdx.x) * P;
+    const int64_t slot0 = static_cast<int64_t>(item) * P;
 
     float M = -INFINITY;
     for (int i = 0; i < P; ++i) M = fmaxf(M, p.ws_ml[((slot0 + i) * BM + row) * 2]);
-    constexpr int H2 = D / 2;   // values per thread
-    float acc[H2];
-#pragma unroll
-    for (int k = 0; k < H2; ++k) acc[k] = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
     for (int i = 0; i < P; ++i) {
         const float2 ml = *reinterpret_cast<const float2 *>(p.ws_ml + ((slot0 + i) * BM + row) * 2);
         const float wi = (M == -INFINITY || ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
         den += wi * ml.y;
-        const float *o = p.ws_o + ((slot0 + i) * BM + row) * D + half * H2;
-#pragma unroll
-        for (int k = 0; k < H2; k += 2) {
-            const float2 v = *reinterpret_cast<const float2 *>(o + k);
-            acc[k] += wi * v.x;
-            acc[k + 1] += wi * v.y;
-        }
+        const float4 v = *reinterpret_cast<const float4 *>(p.ws_o + ((slot0 + i) * BM + row) * D + 4 * c4);
+        acc.x += wi * v.x;
+        acc.y += wi * v.y;
+        acc.z += wi * v.z;
+        acc.w += wi * v.w;
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const int64_t rs = static_cast<int64_t>(p.num_heads) * D;
-    uint16_t *orow = p.out + (qa + q) * rs + head * D + half * H2;
-#pragma unroll
-    for (int k = 0; k < H2; k += 2)
-        *reinterpret_cast<uint32_t *>(orow + k) = pack2<T>(acc[k] * inv, acc[k + 1] * inv);
+    uint16_t *orow = p.out + (qa + q) * rs + head * D + 4 * c4;
+    *reinterpret_cast<uint2 *>(orow) = make_uint2(pack2<T>(acc.x * inv, acc.y * inv), pack2<T>(acc.z * inv, acc.w * inv));
 }
 
 }  // namespace attn

@@ -169,3 +169,42 @@ def test_split_last_wave_matches_whole_items(D):
     check(f64(split[idx]), ref, f"split D={D}", ref_abs=ref_abs)
     check(f64(whole[idx]), ref, f"whole D={D}", ref_abs=ref_abs)
     check(f64(split), f64(whole), f"split vs whole D={D}")
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_small_grid_splits_every_item(D):
+    # 16 query tiles x 4 heads = 64 items, far fewer than the device holds:
+    # every item is split into key ranges and merged
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    inp = gen.prefill_inputs([2024], 4, D, seed=78)
+    assert attn_varlen_fwd_workspace_size(1, 2024, 4, D) > 0
+    d = to_gpu(inp)
+    print(f"[prefill] small grid split D={D}", flush=True)
+    split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=2024)
+    whole = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=2024,
+                            workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), inp["cu_seqlens_q"],
+                                inp["cu_seqlens_k"])
+    check(f64(split), ref, f"small grid split D={D}", ref_abs=ref_abs)
+    check(f64(split), f64(whole), f"small grid split vs whole D={D}")
+
+
+def test_small_grid_split_with_uneven_key_lengths():
+    # the split count is estimated from the query lengths; a sequence with
+    # many more keys, and one with fewer key tiles than ranges, stay exact
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    inp = gen.prefill_inputs([600, 1100], 2, 128, seed=79, seq_lens_k=[4000, 7])
+    assert attn_varlen_fwd_workspace_size(2, 1100, 2, 128) > 0
+    d = to_gpu(inp)
+    print("[prefill] small grid split, uneven keys", flush=True)
+    out = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                          max_seqlen_q=1100)
+    torch.cuda.synchronize()
+    ref = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), inp["cu_seqlens_q"],
+                                inp["cu_seqlens_k"])
+    check(f64(out), ref, "uneven keys", ref_abs=ref_abs)
