@@ -43,6 +43,7 @@ namespace attn {
 
 typedef __attribute__((address_space(3))) void chunk_lds_void;
 typedef unsigned int chunk_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kNonTemporal = 2;   // cache-policy bit of buffer loads: streamed, not kept
 
 constexpr int kChunk = 64;        // tokens per chunk
 constexpr int kChunkDim = 128;    // key_dim = value_dim
@@ -105,7 +106,9 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_delta_out_kernel(ChunkPar
     // lane (r, pos) fetches 16-byte chunk pos ^ f(R) of row R = 4 m + r, so
     // LDS chunk position x of row R holds chunk x ^ f(R).  q and k rows,
     // read 16 bytes per lane: f(R) = R % 8; h_c and v rows, read by
-    // transposing reads: f(R) = 4 (R % 4).
+    // transposing reads: f(R) = 4 (R % 4).  h_c and v are read once and go
+    // non-temporal; the q and k rows stay cached for the other value heads
+    // of the same query head.
     {
         const int rsub = lane >> 4, pos = lane & 15;
         const uint32_t qk_bytes = static_cast<uint32_t>((n - 1) * qrs + D) * 2u;
@@ -127,14 +130,14 @@ __global__ __launch_bounds__(kChunkThreads) void chunk_delta_out_kernel(ChunkPar
         for (int j = 0; j < 8; ++j) {
             const int m = 4 * j + wave_s, R = 4 * m + rsub;
             const uint32_t off = static_cast<uint32_t>(R) * (D * 2u) + 16u * static_cast<uint32_t>(pos ^ (4 * (R & 3)));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsh, (chunk_lds_void *)(h_lds + 4 * m * PITCH), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsh, (chunk_lds_void *)(h_lds + 4 * m * PITCH), 16, off, 0, 0, kNonTemporal);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = 4 * j + wave_s, R = 4 * m + rsub;
             const uint32_t off = static_cast<uint32_t>(R) * static_cast<uint32_t>(vrs * 2) +
                                  16u * static_cast<uint32_t>(pos ^ (4 * (R & 3)));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (chunk_lds_void *)(v_lds + 4 * m * PITCH), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsv, (chunk_lds_void *)(v_lds + 4 * m * PITCH), 16, off, 0, 0, kNonTemporal);
         }
     }
     // a workgroup barrier that waits for no load still in flight; the memory

@@ -18,7 +18,8 @@
 // of each K/V chunk.  The partition's blocks are dealt to the waves round
 // robin; a wave reads a block's K and V chunks with D/32 + D/32 independent
 // 16-byte loads per lane (the next block's loads are issued before the
-// current one is used) and keeps its own online softmax.  Lane l holds, for
+// current one is used; each K/V chunk is read once, so the loads are
+// non-temporal) and keeps its own online softmax.  Lane l holds, for
 // each block,
 //   K: dims 8 (4 c + l / 16) .. +7 of token l % 16   (c = 0 .. D/32 - 1)
 //   V: dim 32 c + l / 2 of tokens 8 (l % 2) .. +7.
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const uint4 z = {0u, 0u, 0u, 0u};
-            kr[c] = ok ? ld16(p.k_cache + base + c * 512 + lane * 8) : z;
-            vr[c] = ok ? ld16(p.v_cache + base + c * 512 + lane * 8) : z;
+            kr[c] = ok ? ld16_stream(p.k_cache + base + c * 512 + lane * 8) : z;
+            vr[c] = ok ? ld16_stream(p.v_cache + base + c * 512 + lane * 8) : z;
         }
         return ok;
     };

@@ -146,6 +146,13 @@ __device__ __forceinline__ float max_halves(float v) {
 
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+// 16-byte load of data read once: marked non-temporal, so it streams
+// through the caches instead of displacing what other waves still reuse
+__device__ __forceinline__ uint4 ld16_stream(const void *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return uint4{v.x, v.y, v.z, v.w};
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 }  // namespace attn
