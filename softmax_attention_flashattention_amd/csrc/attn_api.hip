@@ -49,7 +49,9 @@ int prefill_slots()
 
 // How the work items are launched.  When the last wave of workgroups would
 // be at most half full, its items are split into key ranges (at most 8) that
-// fill it, and a merge kernel combines the ranges.
+// fill it, and a merge kernel combines the ranges; when it would be more than
+// half full, its items are split into the number of ranges that finishes
+// them soonest, if that saves a quarter of an item's time or more.
 struct PrefillPlan {
     int64_t work = 0, whole = 0, parts = 1, grid = 0;
     size_t ws_o_bytes = 0, ws_bytes = 0;
@@ -74,6 +76,29 @@ PrefillPlan plan_prefill(int64_t work, int slots, int bm, int head_dim, int64_t 
         if (key_tiles >= 16 && parts >= 2) {
             pl.parts = parts;
             pl.whole = 0;
+        }
+    } else if (rest > 0 && key_tiles >= 32) {
+        // the last wave is more than half full: split its items into p
+        // ranges of at least 16 key tiles, with p chosen to minimise the
+        // tail's time ceil(tail p / slots) / p (in units of one whole item),
+        // and only when that saves at least a quarter of the unsplit time.
+        // (Shorter ranges lose more to writing and merging the fp32 partial
+        // results of a tail this large than the split gains.)
+        const int64_t whole = (full * slots) / 8 * 8;
+        const int64_t tail = work - whole;
+        int64_t best_p = 1, best_waves = (tail + slots - 1) / slots;   // time: best_waves / best_p items
+        const int64_t pmax = key_tiles / 16 < 8 ? key_tiles / 16 : 8;
+        for (int64_t p = 2; p <= pmax; ++p) {
+            const int64_t waves = (tail * p + slots - 1) / slots;
+            if (waves * best_p < best_waves * p) {
+                best_p = p;
+                best_waves = waves;
+            }
+        }
+        const int64_t base_waves = (tail + slots - 1) / slots;   // unsplit: base_waves / 1
+        if (best_p > 1 && 4 * best_waves <= 3 * best_p * base_waves) {
+            pl.parts = best_p;
+            pl.whole = whole;
         }
     }
     if (pl.parts < 2) {

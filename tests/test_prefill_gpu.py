@@ -193,6 +193,35 @@ def test_small_grid_splits_every_item(D):
     check(f64(split), f64(whole), f"small grid split vs whole D={D}")
 
 
+@pytest.mark.parametrize("H", [26, 10])
+def test_more_than_half_full_wave_is_split(H):
+    # 32 query tiles x H heads at 64 key tiles: with 512 resident workgroups,
+    # 26 heads leave 320 items for a second wave and 10 heads make one wave
+    # of 320; either tail is split into the number of key ranges that
+    # finishes it soonest (3 here) and merged
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    S = 4096
+    inp = gen.prefill_inputs([S], H, 128, seed=80 + H)
+    assert attn_varlen_fwd_workspace_size(1, S, H, 128) > 0
+    d = to_gpu(inp)
+    print(f"[prefill] tail split, {H} heads", flush=True)
+    split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=S)
+    whole = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=S,
+                            workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(H)
+    rows = np.concatenate([[0, S - 1], rng.integers(0, S, 62)])
+    heads = np.concatenate([[H - 1, H - 1], rng.integers(0, H, 62)])
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
+    check(f64(split[idx]), ref, f"tail split H={H}", ref_abs=ref_abs)
+    check(f64(split), f64(whole), f"tail split vs whole H={H}")
+
+
 def test_small_grid_split_with_uneven_key_lengths():
     # the split count is estimated from the query lengths; a sequence with
     # many more keys, and one with fewer key tiles than ranges, stay exact
