@@ -8,11 +8,12 @@
 // Work decomposition.  One workgroup of 4 waves owns a tile of BM = 128
 // query rows of one (sequence, head); each wave owns 32 of those rows.  The
 // workgroup streams the sequence's keys and values in tiles of BN = 64 rows
-// through double-buffered LDS.  For head_dim 128 the tiles go from global
-// memory straight into LDS (buffer loads with the LDS destination bit), laid
-// out unpadded with an XOR swizzle of the 16-byte chunks of each row so that
-// the MFMA operand reads hit distinct banks; head_dim 72 stages them through
-// registers into padded rows.
+// through double-buffered LDS.  The tiles go from global memory straight
+// into LDS (buffer loads with the LDS destination bit).  head_dim 128 lays
+// them out unpadded with an XOR swizzle of the 16-byte chunks of each row so
+// that the MFMA operand reads hit distinct banks; head_dim 72 uses padded
+// rows whose pitch spreads the reads over the banks, with the DMA lanes that
+// would land on pad chunks masked off.
 //
 // Both contractions run on 32x32x16 MFMA with fp32 accumulation, computed
 // transposed so that each lane owns one query row:
@@ -61,7 +62,7 @@ template <int D> struct PrefillShape;
 template <> struct PrefillShape<128> {
     static constexpr int KSTEPS = 8;    // QK^T contraction steps of 16
     static constexpr int DBLK = 4;      // O^T row blocks of 32
-    static constexpr bool DIRECT = true;  // global -> LDS without registers
+    static constexpr bool SWIZZLE = true;  // whole rows per DMA instruction, chunks XOR-swizzled
     static constexpr int KPITCH = 128;  // unpadded rows; chunks XOR-swizzled
     static constexpr int VPITCH = 128;
     static constexpr int ONES_COL = -1;
@@ -70,7 +71,7 @@ template <> struct PrefillShape<128> {
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
     static constexpr int DBLK = 3;      // 72 padded to 96
-    static constexpr bool DIRECT = false;
+    static constexpr bool SWIZZLE = false;  // padded rows; DMA slots on pad chunks masked off
     static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
@@ -103,9 +104,6 @@ void prefill_fwd_kernel(PrefillParams p)
     constexpr int BM = prefill_bm<D>(), BN = kPrefillBN;
     constexpr int KP = S::KPITCH, VP = S::VPITCH;
     constexpr int CH = D / 8;                      // 16-byte chunks per row
-    constexpr int NCH = BN * CH;                   // chunks per K (or V) tile
-    constexpr int PER = (NCH + kPrefillThreads - 1) / kPrefillThreads;
-    constexpr bool DIRECT = S::DIRECT;
 
     // one array per buffer, so that the compiler can tell the buffers apart
     __shared__ __attribute__((aligned(16))) uint16_t k_lds0[BN * KP];
@@ -203,96 +201,89 @@ void prefill_fwd_kernel(PrefillParams p)
         return (rows > 0 && t < t1) ? static_cast<uint32_t>(rows - 1) * row_bytes + D * 2u : 0u;
     };
 
-    // Direct path (head_dim 128): a tile is 16 DMA instructions of 1 KiB
-    // (4 rows; lane i -> bytes 16 i .. 16 i + 15); instruction j of wave w
-    // fills LDS rows RW w + 4 j .. +3, RW = 64 / WAVES.  Row R keeps
+    // Direct path.  A DMA instruction fills 1 KiB of LDS (lane i -> bytes
+    // 16 i .. 16 i + 15), each lane from its own global address.
+    // head_dim 128: a tile is 16 instructions of 4 rows; instruction j of
+    // wave w fills LDS rows RW w + 4 j .. +3, RW = 64 / WAVES.  Row R keeps
     // logical chunk c at position c ^ (R % 16) for K and c ^ 4 (R % 4) for V.
-    constexpr int DJ = 16 / WAVES;      // DMA instructions per wave per tile
-    constexpr int RW = 64 / WAVES;      // tile rows per wave
+    // head_dim 72: the padded tile (KP or VP elements a row) is BN KP / 512
+    // instructions; instruction n = 4 j + w covers the 16-byte slots
+    // 64 n .. 64 n + 63 of the tile, slot s being chunk s % (pitch / 8) of
+    // row s / (pitch / 8); lanes on the pad chunks (>= 9) are masked off,
+    // so the constant pad columns set up below stay as they are.
+    constexpr bool SWZ = S::SWIZZLE;
+    constexpr int NKI = BN * KP / 512, NVI = BN * VP / 512;   // DMA instructions per tile
+    constexpr int DJK = (NKI + WAVES - 1) / WAVES;            // ... per wave (at most)
+    constexpr int DJV = (NVI + WAVES - 1) / WAVES;
+    constexpr int RW = 64 / WAVES;      // tile rows per wave (head_dim 128)
     // (fixed size: a local array sized by a template-dependent constant here
     // makes hipcc drop the kernel's host launch stub for head_dim 128)
     uint32_t dk_off[4] = {0u, 0u, 0u, 0u};
     uint32_t dv_off = 0u;
-    // Staged path (head_dim 72): thread chunks through registers.
-    uint32_t voff[PER];
-    int lds_off_k[PER], lds_off_v[PER];
-    if constexpr (DIRECT) {
+    uint32_t dvp_off[4] = {0u, 0u, 0u, 0u};   // head_dim 72: V slot offsets
+    bool dk_act[4] = {false, false, false, false}, dv_act[4] = {false, false, false, false};
+    if constexpr (SWZ) {
         const int rsub = lane >> 4, pos = lane & 15;
 #pragma unroll
-        for (int j = 0; j < DJ; ++j) {
+        for (int j = 0; j < DJK; ++j) {
             const int R = RW * wave + 4 * j + rsub;
             dk_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (R & 15));
         }
         dv_off = static_cast<uint32_t>(RW * wave + rsub) * row_bytes +
                  16u * static_cast<uint32_t>(pos ^ (4 * (rsub & 3)));
     } else {
+        constexpr int KC = KP / 8, VC = VP / 8;   // 16-byte slots per padded row
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int cidx = tid + i * kPrefillThreads;
-            const int r = cidx / CH, col = (cidx % CH) * 8;
-            voff[i] = static_cast<uint32_t>(r) * row_bytes + static_cast<uint32_t>(col) * 2u;
-            lds_off_k[i] = r * KP + col;
-            lds_off_v[i] = r * VP + col;
+        for (int j = 0; j < DJK; ++j) {
+            const int s = 64 * (4 * j + wave) + lane;
+            dk_off[j] = static_cast<uint32_t>(s / KC) * row_bytes + 16u * static_cast<uint32_t>(s % KC);
+            dk_act[j] = s % KC < CH;
+        }
+#pragma unroll
+        for (int j = 0; j < DJV; ++j) {
+            const int s = 64 * (4 * j + wave) + lane;
+            dvp_off[j] = static_cast<uint32_t>(s / VC) * row_bytes + 16u * static_cast<uint32_t>(s % VC);
+            dv_act[j] = s % VC < CH;
         }
     }
-    // tail loads of head_dim 72 cover only part of the threads (whole waves)
-    auto active = [&](int i) { return NCH % kPrefillThreads == 0 || tid + i * kPrefillThreads < NCH; };
-    uint4 kst[PER], vst[PER];
 
+    // one DMA instruction (number j of this wave) of a K or V tile
+    auto dma_k = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
+        if constexpr (SWZ) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
+        } else {
+            const int n = 4 * j + wave_s;
+            if (n < NKI && dk_act[j])
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(kbuf(par) + 512 * n), 16, dk_off[j],
+                                                         0, 0, 0);
+        }
+    };
+    auto dma_v = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
+        if constexpr (SWZ) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
+                static_cast<int>(4 * j * row_bytes), 0, 0);
+        } else {
+            const int n = 4 * j + wave_s;
+            if (n < NVI && dv_act[j])
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dvp_off[j],
+                                                         0, 0, 0);
+        }
+    };
     auto load_k = [&](int t, auto par) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(k_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
-        if constexpr (DIRECT) {
 #pragma unroll
-            for (int j = 0; j < DJ; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (active(i)) kst[i] = buf_ld16(r, voff[i]);
-        }
+        for (int j = 0; j < DJK; ++j) dma_k(r, par, j);
     };
     auto load_v = [&](int t, auto par) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(v_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
-        if constexpr (DIRECT) {
 #pragma unroll
-            for (int j = 0; j < DJ; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
-                    static_cast<int>(4 * j * row_bytes), 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (active(i)) vst[i] = buf_ld16(r, voff[i]);
-        }
-    };
-    // one DMA instruction (rows RW w + 4 j .. +3) of a K or V tile
-    auto dma_k = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
-    };
-    auto dma_v = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
-            static_cast<int>(4 * j * row_bytes), 0, 0);
-    };
-    auto store_k = [&](auto par) {
-        if constexpr (!DIRECT) {
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (active(i)) st16(kbuf(par) + lds_off_k[i], kst[i]);
-        }
-    };
-    auto store_v = [&](auto par) {
-        if constexpr (!DIRECT) {
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (active(i)) st16(vbuf(par) + lds_off_v[i], vst[i]);
-        }
+        for (int j = 0; j < DJV; ++j) dma_v(r, par, j);
     };
     // all tile data of this iteration in LDS and visible to every wave
     auto tiles_ready = [&]() {
-        if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         __syncthreads();
     };
 
@@ -301,7 +292,7 @@ void prefill_fwd_kernel(PrefillParams p)
     int k_rd[S::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks)
-        k_rd[ks] = DIRECT ? l32 * KP + 8 * ((2 * ks + hi) ^ (l32 & 15)) : l32 * KP + 16 * ks + 8 * hi;
+        k_rd[ks] = SWZ ? l32 * KP + 8 * ((2 * ks + hi) ^ (l32 & 15)) : l32 * KP + 16 * ks + 8 * hi;
     // V^T by transposed reads: row 16 kc + tr_row (+8), column 32 db + tr_col
     const int g16 = lane >> 4;
     const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
@@ -309,7 +300,7 @@ void prefill_fwd_kernel(PrefillParams p)
     int v_rd[S::DBLK];
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db)
-        v_rd[db] = DIRECT ? tr_row * VP + 8 * ((4 * db + (tr_col >> 3)) ^ (4 * (tr_row & 3))) + (tr_col & 7)
+        v_rd[db] = SWZ ? tr_row * VP + 8 * ((4 * db + (tr_col >> 3)) ^ (4 * (tr_row & 3))) + (tr_col & 7)
                           : tr_row * VP + 32 * db + tr_col;
 
     // S^T = K Q^T for the two 32-key blocks of a tile
@@ -411,10 +402,7 @@ void prefill_fwd_kernel(PrefillParams p)
     if (t1 > t0) {
         load_k(t0, P0{});
         load_v(t0, P0{});
-        store_k(P0{});
-        store_v(P0{});
         load_k(t0 + 1, P1{});
-        store_k(P1{});
         tiles_ready();
         compute_s(P0{}, sa);
         mask_tail(t0, sa);
@@ -428,19 +416,18 @@ void prefill_fwd_kernel(PrefillParams p)
     // of the main loop so that the exponentials are not moved past it)
     auto step = [&](int t, auto par, auto npar, const f32x16 (&cur)[2], f32x16 (&nxt)[2], auto masked) {
         // K(t+2) goes to the buffer K(t) left, V(t+1) to the one V(t-1) left.
-        // Direct DMA: one instruction after every other S MFMA (the 2 DJ
-        // instructions issued in one burst stall the wave at issue).
+        // Direct DMA: the instructions spread over the S MFMAs (issued in
+        // one burst they stall the wave at issue).
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_head + static_cast<int64_t>(t + 2) * BN * rs, tile_bytes(t + 2));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_head + static_cast<int64_t>(t + 1) * BN * rs, tile_bytes(t + 1));
-        if constexpr (!DIRECT) {
-            load_k(t + 2, par);
-            load_v(t + 1, npar);
-        }
+        // DMA instruction n of this wave's DJK + DJV goes after S MFMA
+        // floor(n NS / (DJK + DJV)) (every other MFMA for head_dim 128)
         auto dma_slot = [&](int mfma) {
-            if constexpr (DIRECT) {
-                if (mfma % 2 == 0 && mfma / 2 < 2 * DJ) {
-                    const int n = mfma / 2;
-                    if (n < DJ) dma_k(rk, par, n); else dma_v(rv, npar, n - DJ);
+            constexpr int ND = DJK + DJV;
+#pragma unroll
+            for (int n = 0; n < ND; ++n) {
+                if ((n * NS) / ND == mfma) {
+                    if (n < DJK) dma_k(rk, par, n); else dma_v(rv, npar, n - DJK);
                 }
             }
         };
@@ -507,8 +494,6 @@ void prefill_fwd_kernel(PrefillParams p)
             __builtin_amdgcn_sched_barrier(0);
         });
         max_finish(mx, t + 1 < t1);
-        store_k(par);
-        store_v(npar);
         tiles_ready();
     };
     using Unmasked = std::false_type;
