@@ -193,7 +193,9 @@ def shapes_rows(torch, dev, which):
     """Times every row of one operator page's Shapes table (seeded inputs of
     the row's sizes) and prints one JSON line per row: the per-launch time
     of back-to-back launches, the achieved rate against its roofline and the
-    page's production time for context."""
+    page's production time for context.  Rows under 200 us per launch are
+    also timed as 20 calls captured in a HIP graph and replayed (no per-call
+    host path): the device-side rate a launch-bound caller can reach."""
     sys.path.insert(0, os.path.join(ROOT, "tests", "golden"))
     import shapes
     from softmax_attention_flashattention_amd import (attn_chunk_delta_out, attn_paged_decode,
@@ -217,6 +219,21 @@ def shapes_rows(torch, dev, which):
                 return ms / n
             n *= 4
 
+    def graph_timed(call, per_graph=20, reps=20):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * per_graph)
+
     rows = {"prefill": shapes.prefill_rows, "decode": shapes.decode_rows,
             "chunk": shapes.chunk_rows}[which]()
     for r in rows:
@@ -227,34 +244,40 @@ def shapes_rows(torch, dev, which):
             ws = torch.empty(attn_varlen_fwd_workspace_size(1, x["max_seqlen_q"], r["num_heads"],
                                                             r["head_dim"]), dtype=torch.uint8,
                              device=dev)
-            ms = timed(lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"],
-                                               d["cu_seqlens_k"], max_seqlen_q=x["max_seqlen_q"],
-                                               out=out, workspace=ws))
+            call = lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"],
+                                           d["cu_seqlens_k"], max_seqlen_q=x["max_seqlen_q"],
+                                           out=out, workspace=ws)
             work = prefill_flops(x)
-            rate, unit, peak = work / (ms * 1e-3) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+            unit, peak = "TFLOP/s", PEAK_BF16_TFLOPS
         elif which == "decode":
             x = gen.decode_inputs(r["num_seqs"], r["ctx_len"], r["num_query_heads"],
                                   r["num_kv_heads"], r["head_size"], seed=3000 + r["row"],
                                   dtype=r["dtype"])
             d = {k: v.to(dev) for k, v in x.items()}
             out = torch.empty_like(d["query"])
-            ms = timed(lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"],
-                                                 d["block_tables"], d["seq_lens"], out=out))
+            call = lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"],
+                                             d["block_tables"], d["seq_lens"], out=out)
             work = decode_bytes(x)
-            rate, unit, peak = work / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+            unit, peak = "GB/s", PEAK_HBM_GBS
         else:
             x = gen.chunk_inputs(r["batch_size"], r["token_count"], r["num_q_heads"],
                                  r["num_v_heads"], seed=4000 + r["row"])
             d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
             out = torch.empty_like(d["v"])
-            ms = timed(lambda: attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"], out=out))
+            call = lambda: attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"], out=out)
             work = chunk_bytes(x)
-            rate, unit, peak = work / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+            unit, peak = "GB/s", PEAK_HBM_GBS
+        scale = 1e12 if which == "prefill" else 1e9
+        ms = timed(call)
+        rate = work / (ms * 1e-3) / scale
+        gms = graph_timed(call) if ms < 0.2 else None
         sizes = {k: v for k, v in r.items() if k not in ("t_sol_us", "t_prod_us")}
-        print(json.dumps({"shapes": which, **sizes, "us_per_launch": round(ms * 1e3, 2),
-                          "achieved": round(rate, 1), "unit": unit,
-                          "frac": round(rate / peak, 4), "page_t_prod_us": r["t_prod_us"]}),
-              flush=True)
+        line = {"shapes": which, **sizes, "us_per_launch": round(ms * 1e3, 2),
+                "achieved": round(rate, 1), "unit": unit, "frac": round(rate / peak, 4),
+                "graph_us_per_launch": None if gms is None else round(gms * 1e3, 2),
+                "graph_frac": None if gms is None else round(work / (gms * 1e-3) / scale / peak, 4),
+                "page_t_prod_us": r["t_prod_us"]}
+        print(json.dumps(line), flush=True)
         del x, d, out
 
 

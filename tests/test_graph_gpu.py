@@ -1,0 +1,85 @@
+"""The entry points captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed: every replay must reproduce the eager call's output bit for bit.
+
+Launch-bound callers (small shapes, serving loops) replay captured calls
+instead of paying the per-call host path each time.  A call enqueues its
+kernels on the caller's stream and does no host synchronisation, device
+allocation or memset, so it can be captured as it is (prefill needs
+`max_seqlen_q` passed in: deriving it reads the sequence bounds back to the
+host).  Each case uses the work split that adds a second kernel (prefill key
+ranges and their merge, decode context partitions and their merge), and
+each replay is checked with eager calls and synchronisations in between.
+"""
+import pytest
+import torch
+
+from parity import to_gpu
+from softmax_attention_flashattention_amd import (attn_chunk_delta_out, attn_paged_decode,
+                                                  attn_varlen_fwd, inputs as gen)
+
+pytestmark = pytest.mark.gpu
+
+
+def replay_matches_eager(call, what, reps=4):
+    print(f"[graph] {what}", flush=True)
+    eager = call().clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = call()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        out.fill_(7.0)           # the replay must rewrite every element
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"{what}: replay {i} differs from the eager call"
+        again = call()           # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager), f"{what}: eager call after replay {i} differs"
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_prefill_split_and_merge_replays(D):
+    # 16 query tiles x 4 heads: every item is split into key ranges, so the
+    # graph holds the prefill kernel and the merge kernel
+    inp = gen.prefill_inputs([2024], 4, D, seed=90 + D)
+    d = to_gpu(inp)
+    replay_matches_eager(
+        lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                max_seqlen_q=2024),
+        f"prefill 2024 x 4 heads, D={D}")
+
+
+def test_prefill_varlen_batch_replays():
+    inp = gen.prefill_inputs([300, 1, 777], 2, 128, seed=93)
+    d = to_gpu(inp)
+    replay_matches_eager(
+        lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                max_seqlen_q=777),
+        "prefill varlen batch")
+
+
+def test_decode_partitions_and_merge_replay():
+    lens = [1000, 333, 17, 0, 512, 1]
+    inp = gen.decode_inputs(6, 1000, 8, 4, 128, seed=94, seq_lens=lens)
+    d = to_gpu(inp)
+    replay_matches_eager(
+        lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["seq_lens"], partition_size=112),
+        "decode, 112-token partitions")
+
+
+def test_decode_workload_replays():
+    d = to_gpu(gen.workload_inputs("decode_b256_ctx64_h16_kv16_d128"))
+    replay_matches_eager(
+        lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["seq_lens"]),
+        "decode 256 x 64")
+
+
+def test_chunk_output_replays():
+    x = gen.chunk_inputs(2, 300, 2, 4, seed=95)
+    d = to_gpu(x)
+    replay_matches_eager(
+        lambda: attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"]),
+        "chunk output 2 x 300 tokens")
