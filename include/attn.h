@@ -15,10 +15,13 @@
  *
  * Conventions shared by every entry point
  *  - Every tensor pointer is device memory owned by the caller.  The library
- *    never allocates, frees or synchronises; it writes only `out` and, for
- *    decode, the caller's `workspace`.
+ *    never allocates, frees or synchronises; it writes only `out` and the
+ *    caller's `workspace` (prefill's key-range split, decode's context
+ *    partitions).
  *  - Calls enqueue their kernels on `stream` (a hipStream_t; NULL is the null
- *    stream) and return at once.  They never read device memory on the host.
+ *    stream) and return at once.  They never read device memory on the host
+ *    and issue no memset, so a call can be captured into a HIP graph and
+ *    replayed (the captured pointers and sizes are reused as they are).
  *  - 16-bit tensors are contiguous, row-major, and 16-byte aligned; int32
  *    index arrays are contiguous and 4-byte aligned.
  *  - Calls return an attn_status and never print, throw or abort.  Argument
