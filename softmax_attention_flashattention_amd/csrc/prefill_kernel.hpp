@@ -432,6 +432,13 @@ void prefill_fwd_kernel(PrefillParams p)
             }
         };
         __builtin_amdgcn_sched_barrier(0);
+        // Wave priority by phase: the two workgroups sharing a SIMD drift
+        // apart, so one wave is often in its S phase (MFMAs plus most of the
+        // exponentials) while the other is in its PV phase or at the barrier.
+        // Issuing the S phase first, then PV, then the rest measured 1-2%
+        // faster than equal priorities.
+        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_sched_barrier(0);
 
         // The NS MFMAs of S(t+1) = K(t+1) Q^T, in the order ks outer, kb2
         // inner (two independent accumulator chains), each K operand read KD
@@ -487,12 +494,18 @@ void prefill_fwd_kernel(PrefillParams p)
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (decltype(masked)::value) mask_tail(t + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
         float mx = -INFINITY;
         pv(par, pw, [&](int j) {
             if (j < NB) exp_pairs(NA + ((16 - NA) * j) / NB, NA + ((16 - NA) * (j + 1)) / NB);
             mx = max_part(nxt, j, NPV, mx);
             __builtin_amdgcn_sched_barrier(0);
         });
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
         max_finish(mx, t + 1 < t1);
         tiles_ready();
     };
