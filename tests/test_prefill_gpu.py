@@ -144,6 +144,25 @@ def test_workload_sampled_rows(name):
     sampled_check(name)
 
 
+def test_workload_s16742_split_items_sampled():
+    # the benchmark's launch: 131 query tiles x 32 heads = 4192 items on 512
+    # resident workgroups, so the last 96 items (head 31, query rows from
+    # 35 * 128 on) run as key ranges merged by log-sum-exp; sample them
+    name = "prefill_s16742_h32_d128"
+    inp = gen.workload_inputs(name)
+    print(f"[prefill] {name} split items", flush=True)
+    out = run(inp)
+    S = inp["q"].shape[0]
+    rng = np.random.default_rng(11)
+    rows = np.concatenate([[35 * 128, 35 * 128 + 127, S - 1], rng.integers(35 * 128, S, 61)])
+    heads = np.full(rows.size, 31)
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
+    check(got, ref, f"{name} split items", ref_abs=ref_abs)
+
+
 @pytest.mark.parametrize("D", [72, 128])
 def test_split_last_wave_matches_whole_items(D):
     # 516 heads x 1 query tile: one full wave of workgroups plus a few items,
