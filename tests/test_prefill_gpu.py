@@ -144,6 +144,46 @@ def test_workload_sampled_rows(name):
     sampled_check(name)
 
 
+def test_many_sequences_of_random_lengths():
+    # 40 sequences, query lengths 0..700 and key lengths 0..900: most query
+    # tiles of the grid (sized by the longest sequence) exit at once
+    rng = np.random.default_rng(5)
+    lq = [int(x) for x in rng.integers(0, 701, 40)]
+    lk = [int(x) for x in rng.integers(0, 901, 40)]
+    lq[3], lk[3] = 700, 900
+    inp = gen.prefill_inputs(lq, 2, 128, seed=61, seq_lens_k=lk)
+    full_check(inp, "40 sequences")
+
+
+def test_varlen_batch_with_split_tail():
+    # 3 sequences x 4 heads, up to 32 query tiles: 384 items fill more than
+    # half of the 512 resident workgroups, so every item is split into key
+    # ranges, each over its own sequence's keys
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    lens = [3000, 1500, 4096]
+    inp = gen.prefill_inputs(lens, 4, 128, seed=62, seq_lens_k=[2500, 4100, 4096])
+    assert attn_varlen_fwd_workspace_size(3, 4096, 4, 128) > 0
+    d = to_gpu(inp)
+    print("[prefill] varlen batch, split tail", flush=True)
+    split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=4096)
+    whole = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=4096,
+                            workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    starts = np.cumsum([0] + lens)
+    rows = np.concatenate([starts[i] + np.concatenate([[0, lens[i] - 1], rng.integers(0, lens[i], 20)])
+                           for i in range(3)])
+    heads = rng.integers(0, 4, rows.size)
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
+    check(f64(split[idx]), ref, "varlen split", ref_abs=ref_abs)
+    check(f64(split), f64(whole), "varlen split vs whole")
+
+
 def test_workload_s16742_split_items_sampled():
     # the benchmark's launch: 131 query tiles x 32 heads = 4192 items on 512
     # resident workgroups, so the last 96 items (head 31, query rows from
