@@ -399,6 +399,11 @@ void prefill_fwd_kernel(PrefillParams p)
     // those loads fetch nothing and return zeros; the extra S block of the
     // last iteration is discarded.
     f32x16 sa[2], sb[2];
+    constexpr int KD = 3;   // K operands read this many MFMAs ahead
+    s16x8 kq_pre[KD];       // the first KD K operands of a step, read before it starts
+    auto kop_at = [&](const uint16_t *kt, int i) {
+        return *reinterpret_cast<const s16x8 *>(kt + 32 * (i & 1) * KP + k_rd[i >> 1]);
+    };
     if (t1 > t0) {
         load_k(t0, P0{});
         load_v(t0, P0{});
@@ -408,6 +413,8 @@ void prefill_fwd_kernel(PrefillParams p)
         mask_tail(t0, sa);
         max_finish(max_part(sa, 0, 1, -INFINITY), true);
         __syncthreads();   // K buffer 0 is refilled at the start of the first iteration
+#pragma unroll
+        for (int i = 0; i < KD; ++i) kq_pre[i] = kop_at(k_lds1, i);
     }
 
     constexpr int NS = 2 * S::KSTEPS;   // S MFMAs per tile (two 32-key blocks)
@@ -446,13 +453,10 @@ void prefill_fwd_kernel(PrefillParams p)
         // of tile t: exponentials, 16-bit packing and row sums of its 16 value
         // pairs.
         const uint16_t *kt = kbuf(npar);
-        auto kop = [&](int i) {
-            return *reinterpret_cast<const s16x8 *>(kt + 32 * (i & 1) * KP + k_rd[i >> 1]);
-        };
-        constexpr int KD = 3;   // K operands read this many MFMAs ahead
+        auto kop = [&](int i) { return kop_at(kt, i); };
         s16x8 kq[KD + 1];
 #pragma unroll
-        for (int i = 0; i < KD; ++i) kq[i] = kop(i);
+        for (int i = 0; i < KD; ++i) kq[i] = kq_pre[i];   // read during the previous step
         const f32x16 zero = {};
         uint32_t pw[16];
         // exponentials, 16-bit packing and row sums of value pairs [pb, pe)
@@ -498,16 +502,31 @@ void prefill_fwd_kernel(PrefillParams p)
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
         float mx = -INFINITY;
+        // The end-of-step barrier sits before the last BAR_AT PV MFMAs: by
+        // then every V(t) operand read has been issued (PD ahead), so once
+        // they have landed and this wave's tile DMA is complete, all waves
+        // may hand the buffers over.  The first KD operands of K(t+2), which
+        // the next step starts with, are then read while those MFMAs run.
+        constexpr int BAR_AT = 3;
+        static_assert(BAR_AT <= 4, "the barrier must follow the last V^T operand read (PD = 3 ahead)");
         pv(par, pw, [&](int j) {
             if (j < NB) exp_pairs(NA + ((16 - NA) * j) / NB, NA + ((16 - NA) * (j + 1)) / NB);
             mx = max_part(nxt, j, NPV, mx);
             __builtin_amdgcn_sched_barrier(0);
+            if (j == NPV - BAR_AT) {
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                const uint16_t *kn = kbuf(par);    // K(t+2), complete and visible now
+#pragma unroll
+                for (int i = 0; i < KD; ++i) kq_pre[i] = kop_at(kn, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         });
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         max_finish(mx, t + 1 < t1);
-        tiles_ready();
     };
     using Unmasked = std::false_type;
     using Masked = std::true_type;
