@@ -75,6 +75,9 @@ typedef enum attn_dtype {
  *  max_seqlen_q   an upper bound on cu_seqlens_q[i+1] - cu_seqlens_q[i]; it
  *                 sizes the grid, so query rows past it are not computed
  *  head_dim       72 or 128 (others return ATTN_ERR_UNSUPPORTED)
+ *  num_heads      num_heads * head_dim < 2^25 (a key tile of 64 rows is
+ *                 addressed with 32-bit byte offsets); larger returns
+ *                 ATTN_ERR_INVALID_ARG
  *  scale          finite; the pages use head_dim^-1/2
  *  workspace      optional device memory, 256-byte aligned, of
  *                 attn_varlen_fwd_workspace_size(...) bytes.  When the work
@@ -183,6 +186,8 @@ size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_head
  *            dtype: the state each chunk starts from
  *  g         [batch, tokens, num_heads] float32 (log gates), 4-byte aligned
  *  key_dim, value_dim  128; chunk_size 64 (others: ATTN_ERR_UNSUPPORTED)
+ *  num_q_heads, num_heads  below 131072 each (one chunk of rows is
+ *            addressed with 32-bit offsets); larger: ATTN_ERR_INVALID_ARG
  *  scale     finite; the page uses key_dim^-1/2
  *  out       [batch, tokens, num_heads, value_dim], dtype; every row written
  *

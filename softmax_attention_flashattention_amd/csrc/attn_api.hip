@@ -197,6 +197,9 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (head_dim != 72 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    // the kernel addresses a key tile with 32-bit byte offsets
+    if (static_cast<int64_t>(num_heads) * head_dim * 2 * attn::kPrefillBN > UINT32_MAX)
+        return ATTN_ERR_INVALID_ARG;
     if (num_seqs == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
     if (!q || !cu_seqlens_q || !cu_seqlens_k || !out) return ATTN_ERR_INVALID_ARG;
     if ((!k || !v) && total_k > 0) return ATTN_ERR_INVALID_ARG;   // k, v may be empty
@@ -342,9 +345,11 @@ int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void
         return ATTN_ERR_INVALID_ARG;
     const int64_t num_chunks = (static_cast<int64_t>(tokens) + chunk_size - 1) / chunk_size;
     const int64_t grid = static_cast<int64_t>(batch) * num_chunks * num_heads;
-    // the kernel's buffer offsets are 32-bit: one chunk of v rows must span < 4 GiB
+    // the kernel's buffer offsets are 32-bit: one chunk of q, k or v rows must
+    // span less than 2 GiB
     const int64_t v_span = static_cast<int64_t>(chunk_size) * num_heads * value_dim * 2;
-    if (grid > INT32_MAX || v_span > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+    const int64_t qk_span = static_cast<int64_t>(chunk_size) * num_q_heads * key_dim * 2;
+    if (grid > INT32_MAX || v_span > INT32_MAX || qk_span > INT32_MAX) return ATTN_ERR_INVALID_ARG;
 
     attn::ChunkParams p;
     p.q = static_cast<const uint16_t *>(q);

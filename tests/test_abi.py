@@ -76,6 +76,9 @@ def test_varlen_argument_errors(lib):
     assert varlen(lib, k=FAKE + 8) == INVALID          # not 16-byte aligned
     assert varlen(lib, cu_q=FAKE + 2) == INVALID       # not 4-byte aligned
     assert varlen(lib, ws=FAKE + 16, ws_bytes=1 << 20) == INVALID   # not 256-byte aligned
+    # a 64-row key tile must be addressable with 32-bit byte offsets
+    assert varlen(lib, num_heads=(1 << 25) // 128) == INVALID
+    assert varlen(lib, num_heads=(1 << 25) // 72 + 1, head_dim=72) == INVALID
 
 
 def test_varlen_empty_work_is_ok_without_launch(lib):
@@ -155,6 +158,9 @@ def test_chunk_argument_errors(lib):
     assert chunk(lib, g=None) == INVALID
     assert chunk(lib, out=FAKE + 8) == INVALID         # not 16-byte aligned
     assert chunk(lib, g=FAKE + 2) == INVALID           # not 4-byte aligned
+    # one chunk of q/k or v rows must be addressable with 32-bit offsets
+    assert chunk(lib, hv=131072) == INVALID
+    assert chunk(lib, hq=131072) == INVALID
 
 
 def test_chunk_empty_input_is_ok_without_launch(lib):
