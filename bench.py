@@ -15,8 +15,10 @@ back after the step loop (a lone 26-us call's event pair would also time its
 dispatch).
 
 Printed: one JSON line with prefill TFLOP/s (the headline value), decode
-GB/s, both against MI355X roofline peaks, and the CPU oracle's rate on a
-bounded sample (rank 0, one GPU).  Only one GPU is used: --gpus above 1 exits
+GB/s, both against MI355X roofline peaks, the CPU oracle's rate on a bounded
+sample (rank 0, one GPU), and under "page_context" the pages' own T_SOL and
+T_Prod for the same workloads (hardware labelled only "XPU-A"; context, not a
+target) beside this run's per-launch times.  Only one GPU is used: --gpus above 1 exits
 with a message.
 """
 import argparse
@@ -281,6 +283,29 @@ def shapes_rows(torch, dev, which):
         del x, d, out
 
 
+def page_context(p_host):
+    """The pages' own times for the timed workloads (Shapes tables stored under
+    tests/golden): T_SOL on hardware the pages label only "XPU-A", T_Prod on
+    unstated hardware.  Context, never a target."""
+    sys.path.insert(0, os.path.join(ROOT, "tests", "golden"))
+    import shapes
+    S, H, D = int(p_host["max_seqlen_q"]), int(p_host["q"].shape[1]), int(p_host["q"].shape[2])
+    pre = [r for r in shapes.prefill_rows()
+           if (r["seq_len"], r["num_heads"], r["head_dim"]) == (S, H, D)]
+    dec = [r for r in shapes.decode_rows()
+           if (r["num_seqs"], r["ctx_len"], r["num_query_heads"], r["num_kv_heads"],
+               r["head_size"]) == (256, 64, 16, 16, 128)]
+    chk = [r for r in shapes.chunk_rows()
+           if (r["token_count"], r["num_v_heads"], r["num_q_heads"]) == (14807, 32, 16)]
+    ctx = {"hardware": "XPU-A (name missing from the pages); T_Prod hardware unstated",
+           "note": "context only, not a target"}
+    for key, rows in (("prefill", pre), ("decode", dec), ("chunk", chk)):
+        if rows:
+            ctx[key] = {"page_row": rows[0]["row"], "t_sol_us": rows[0]["t_sol_us"],
+                        "t_prod_us": rows[0]["t_prod_us"]}
+    return ctx
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,11 +512,19 @@ def main():
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
         "kernel_source_hash": src_hash,
+        "page_context": page_context(p_host),
     }
+    # this run's per-launch times beside the pages' (context only)
+    for key, us, on in (("prefill", pre_avg * 1e3, do_prefill), ("decode", dec_avg * 1e3, do_decode),
+                        ("chunk", chunk_avg * 1e3, do_chunk)):
+        if on and key in result["page_context"]:
+            result["page_context"][key]["this_run_us"] = round(us, 2)
     if args.only is not None:
         result["only"] = args.only
     if args.cpu_budget > 0 and args.only is None:
         result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        if p_name == PREFILL and tflops > 0:
+            result["cpu_baseline"]["gpu_over_cpu"] = round(tflops / result["cpu_baseline"]["value"], 1)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
