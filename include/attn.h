@@ -73,7 +73,9 @@ typedef enum attn_dtype {
  *                 cu_seqlens_q[num_seqs] <= total_q
  *  cu_seqlens_k   [num_seqs + 1] int32, the same rules against total_k
  *  max_seqlen_q   an upper bound on cu_seqlens_q[i+1] - cu_seqlens_q[i]; it
- *                 sizes the grid, so query rows past it are not computed
+ *                 sizes the grid (whole tiles of query rows), so a segment
+ *                 longer than it is a caller error: its rows past the last
+ *                 tile the bound covers are left unwritten
  *  head_dim       72 or 128 (others return ATTN_ERR_UNSUPPORTED)
  *  num_heads      num_heads * head_dim < 2^25 (a key tile of 64 rows is
  *                 addressed with 32-bit byte offsets); larger returns

@@ -76,6 +76,29 @@ def test_rows_outside_segments_are_untouched(D):
 
 
 @pytest.mark.parametrize("D", [72, 128])
+def test_segment_longer_than_max_seqlen_q_writes_nothing_wrong(D):
+    # a caller error: max_seqlen_q = 100 below a 300-row segment.  Rows under
+    # the bound are computed; every other row is either left as it was or
+    # holds its correct value (whole query tiles are computed) -- nothing else.
+    inp = gen.prefill_inputs([300, 40], 2, D, seed=11)
+    d = to_gpu(inp)
+    out = torch.full_like(d["q"], SENTINEL)
+    attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=100, out=out)
+    torch.cuda.synchronize()
+    o = f64(out)
+    ref, ref_abs = refs(inp)
+    under = np.r_[0:100, 300:340]
+    check(o[under], ref[under], f"rows under the bound D={D}", ref_abs=ref_abs[under])
+    rest = o[100:300]
+    untouched = np.all(rest == SENTINEL, axis=(1, 2))
+    assert untouched.any(), "rows far past the bound were written"
+    written = ~untouched
+    check(rest[written], ref[100:300][written], f"rows past the bound D={D}",
+          ref_abs=ref_abs[100:300][written])
+
+
+@pytest.mark.parametrize("D", [72, 128])
 def test_scaled_values_tighten_the_floor(D):
     # out is linear in V and a power-of-two scale is exact in bf16; with V
     # scaled up the output errors are judged by the scale-free bar 2 only.
