@@ -233,7 +233,8 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     p.split_parts = static_cast<int>(pl.parts);
     p.ws_o = pl.parts > 1 ? static_cast<float *>(workspace) : nullptr;
     p.ws_ml = pl.parts > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.ws_o_bytes) : nullptr;
-    p.scale_log2e = scale * attn::kLog2e;
+    p.scale_log2e = std::fabs(scale) * attn::kLog2e;
+    p.negate_q = scale < 0.f ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (head_dim == 128)

@@ -28,8 +28,12 @@
 // {4-7, 12-15} in lanes 32-63); V^T is read in that same order, which the
 // transposed LDS read produces directly from a row-major V tile.
 //
-// Softmax runs in the base-2 domain: with c = scale * log2(e), the running
+// Softmax runs in the base-2 domain: with c = |scale| * log2(e), the running
 // max m is kept for c*s and p = exp2(c*s - m), alpha = exp2(m_old - m_new).
+// A negative scale is applied by negating Q as it is loaded (exact in 16
+// bits), so c >= 0 and the max of the raw scores is the max of c*s.  Keys past
+// the end of the sequence get weight 0 by selection, which holds for c = 0
+// as well (where c * -inf would be NaN).
 //
 // head_dim 72 pads the QK^T contraction to 80 (five k-steps of 16; the K pad
 // columns are zero) and the V^T row blocks to 96; column 72 of the V tile
@@ -55,7 +59,8 @@ struct PrefillParams {
     int split_parts;  // items [whole_work, total_work) run as this many key ranges
     float *ws_o;      // split items: [(item - whole_work) * split_parts + part][BM][D], unnormalised O
     float *ws_ml;     // split items: [... same slot ...][BM][2]: running max (log2 domain), row sum
-    float scale_log2e;
+    float scale_log2e;  // |scale| * log2(e)
+    int negate_q;       // scale < 0: Q enters the products negated
 };
 
 template <int D> struct PrefillShape;
@@ -186,6 +191,12 @@ void prefill_fwd_kernel(PrefillParams p)
         const int d0 = 16 * ks + 8 * hi;
         uint4 v4 = {0u, 0u, 0u, 0u};
         if (qrow < Sq && d0 < D) v4 = ld16(p.q + (qa + qrow) * rs + head * D + d0);
+        if (p.negate_q) {   // flip the sign bit of each 16-bit element
+            v4.x ^= 0x80008000u;
+            v4.y ^= 0x80008000u;
+            v4.z ^= 0x80008000u;
+            v4.w ^= 0x80008000u;
+        }
         qreg[ks] = __builtin_bit_cast(s16x8, v4);
     }
 
@@ -465,8 +476,17 @@ void prefill_fwd_kernel(PrefillParams p)
 #pragma unroll
             for (int pi = pb; pi < pe; ++pi) {
                 const int kb = pi >> 3, r = 2 * (pi & 7);
-                const float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], c, -m_run));
-                const float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c, -m_run));
+                float p0 = fast_exp2(__builtin_fmaf(cur[kb][r], c, -m_run));
+                float p1 = fast_exp2(__builtin_fmaf(cur[kb][r + 1], c, -m_run));
+                if constexpr (decltype(masked)::value) {
+                    // tile t may be the partial last one (peeled steps only):
+                    // keys past the end get weight 0 whatever the scale
+                    if (t * BN + BN > Sk) {
+                        const int key = t * BN + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        p0 = key < Sk ? p0 : 0.f;
+                        p1 = key + 1 < Sk ? p1 : 0.f;
+                    }
+                }
                 pw[pi] = pack2<T>(p0, p1);
                 if constexpr (S::ONES_COL < 0) {
                     // the empty asm keeps each sum in its slice (otherwise the

@@ -98,6 +98,35 @@ def test_segment_longer_than_max_seqlen_q_writes_nothing_wrong(D):
           ref_abs=ref_abs[100:300][written])
 
 
+def scaled_check(inp, scale, what):
+    d = to_gpu(inp)
+    out = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                          max_seqlen_q=inp["max_seqlen_q"], scale=scale)
+    torch.cuda.synchronize()
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    ref = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], *args, scale=scale)
+    ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), *args, scale=scale)
+    m = ~np.isnan(ref)
+    check(f64(out)[m], ref[m], what, ref_abs=ref_abs[m])
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+@pytest.mark.parametrize("D", [72, 128])
+def test_zero_and_negative_scale(D, scale):
+    # the definition holds for any finite scale: 0 gives the mean of the
+    # segment's values, a negative one favours the least similar keys.  Key
+    # lengths leave a partial last key tile, where the kernel masks keys.
+    inp = gen.prefill_inputs([100, 37, 200], 2, D, seed=51, seq_lens_k=[70, 129, 5])
+    scaled_check(inp, scale, f"scale {scale} D={D}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_zero_and_negative_scale_on_split_items(scale):
+    # 2024 tokens x 4 heads: every work item is split into key ranges and merged
+    inp = gen.prefill_inputs([2024], 4, 128, seed=53, seq_lens_k=[2000])
+    scaled_check(inp, scale, f"scale {scale} split items")
+
+
 @pytest.mark.parametrize("D", [72, 128])
 def test_scaled_values_tighten_the_floor(D):
     # out is linear in V and a power-of-two scale is exact in bf16; with V
