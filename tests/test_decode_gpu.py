@@ -61,6 +61,15 @@ def test_ragged_and_empty_contexts():
     assert torch.count_nonzero(o[12]).item() == 0 and torch.count_nonzero(o[13]).item() == 0
 
 
+def test_sharp_attention_over_a_long_context():
+    # query x 32 (exact in bf16): scores spread over hundreds of log2 units
+    # and the split-K partitions see very different maxima
+    inp = gen.decode_inputs(8, 1000, 8, 2, 128, seed=57)
+    inp["query"] = (inp["query"].float() * 32).to(torch.bfloat16)
+    full_check(inp, "sharp, one partition")
+    full_check(inp, "sharp, 64-token partitions", partition_size=64)
+
+
 def test_one_token_context_returns_value_row_exactly():
     inp = gen.decode_inputs(8, 1, 4, 2, 128, seed=7)
     per = gen.permute_blocks(inp, seed=8)

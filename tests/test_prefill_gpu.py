@@ -110,6 +110,20 @@ def scaled_check(inp, scale, what):
     check(f64(out)[m], ref[m], what, ref_abs=ref_abs[m])
 
 
+@pytest.mark.parametrize("D", [72, 128])
+def test_sharp_attention_with_growing_maxima(D):
+    # q x 32 (exact): scores spread over hundreds of log2 units, so the
+    # running max grows past the lazy-rescale threshold on many tiles and
+    # most weights underflow; keys are ordered so maxima keep rising
+    inp = gen.prefill_inputs([700, 90], 2, D, seed=55)
+    inp["q"] = (inp["q"].float() * 32).to(torch.bfloat16)
+    k = inp["k"].clone()
+    norms = k[:700].float().norm(dim=2).sum(dim=1)
+    k[:700] = k[:700][torch.argsort(norms)]          # growing key norms in sequence 0
+    inp["k"] = k
+    full_check(inp, f"sharp D={D}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3])
 @pytest.mark.parametrize("D", [72, 128])
 def test_zero_and_negative_scale(D, scale):
