@@ -18,14 +18,12 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int launch_status() { return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-template <int D> constexpr int prefill_rows() { return attn::prefill_bm<D>(); }
-
-template <int D, typename T>
+template <int D, typename T, int W>
 int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
 {
-    constexpr int BM = prefill_rows<D>();
-    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T>), dim3(static_cast<unsigned>(grid)),
-                       dim3(attn::prefill_threads<D>()), 0, stream, p);
+    constexpr int BM = attn::prefill_bm(W);
+    hipLaunchKernelGGL((attn::prefill_fwd_kernel<D, T, W>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::prefill_threads(W)), 0, stream, p);
     int rc = launch_status();
     if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
     hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>),
@@ -36,15 +34,45 @@ int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t strea
 
 // Work items that fit the device at once: compute units x resident
 // workgroups per unit (0 when the runtime cannot tell, e.g. no device).
-template <int D>
+template <int D, int W>
 int prefill_slots()
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, attn::prefill_fwd_kernel<D, attn::Bf16>, attn::prefill_threads<D>(), 0);
+        &per_cu, attn::prefill_fwd_kernel<D, attn::Bf16, W>, attn::prefill_threads(W), 0);
     return e == hipSuccess ? cus * per_cu : 0;
+}
+
+// Waves per workgroup for a call, and the resulting work items and slots.
+// head_dim 72 takes 8 waves (256 query rows) when those items fill every
+// slot at least once; smaller grids keep 4 (the shorter Shapes rows ran up
+// to 30% slower with 8: fewer, longer work items).
+struct PrefillShapeChoice {
+    int waves = 4, bm = 128, slots = 0;
+    int64_t qtiles = 0, work = 0;
+};
+
+PrefillShapeChoice choose_prefill(int64_t num_seqs, int64_t max_seqlen_q, int64_t num_heads, int head_dim)
+{
+    PrefillShapeChoice c;
+    if (head_dim == 72) {
+        const int slots8 = prefill_slots<72, 8>();
+        const int64_t work8 = num_seqs * num_heads * ((max_seqlen_q + 255) / 256);
+        if (slots8 > 0 && work8 >= slots8) {
+            c.waves = 8;
+            c.slots = slots8;
+        } else {
+            c.slots = prefill_slots<72, 4>();
+        }
+    } else {
+        c.slots = prefill_slots<128, 4>();
+    }
+    c.bm = attn::prefill_bm(c.waves);
+    c.qtiles = (max_seqlen_q + c.bm - 1) / c.bm;
+    c.work = num_seqs * num_heads * c.qtiles;
+    return c;
 }
 
 // How the work items are launched.  When the last wave of workgroups would
@@ -177,12 +205,9 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, in
 {
     if (num_seqs <= 0 || max_seqlen_q <= 0 || num_heads <= 0) return 0;
     if (head_dim != 72 && head_dim != 128) return 0;
-    const int bm = head_dim == 128 ? prefill_rows<128>() : prefill_rows<72>();
-    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
-    const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
-    const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
+    const PrefillShapeChoice c = choose_prefill(num_seqs, max_seqlen_q, num_heads, head_dim);
     const int64_t key_tiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBN - 1) / attn::kPrefillBN;
-    return plan_prefill(work, slots, bm, head_dim, key_tiles).ws_bytes;
+    return plan_prefill(c.work, c.slots, c.bm, head_dim, key_tiles).ws_bytes;
 }
 
 int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
@@ -207,13 +232,15 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
         !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
         return ATTN_ERR_INVALID_ARG;
 
-    const int bm = head_dim == 128 ? prefill_rows<128>() : prefill_rows<72>();
-    const int64_t qtiles = (static_cast<int64_t>(max_seqlen_q) + bm - 1) / bm;
-    const int64_t work = static_cast<int64_t>(num_seqs) * num_heads * qtiles;
-    if (work > INT32_MAX / 8) return ATTN_ERR_INVALID_ARG;
-    const int slots = head_dim == 128 ? prefill_slots<128>() : prefill_slots<72>();
+    // (work items at 128 rows bound the count for either workgroup size)
+    const int64_t work128 = static_cast<int64_t>(num_seqs) * num_heads * ((max_seqlen_q + 127) / 128);
+    if (work128 > INT32_MAX / 8) return ATTN_ERR_INVALID_ARG;
+    const PrefillShapeChoice c = choose_prefill(num_seqs, max_seqlen_q, num_heads, head_dim);
+    const int bm = c.bm;
+    const int64_t qtiles = c.qtiles;
+    const int64_t work = c.work;
     const int64_t key_tiles = (static_cast<int64_t>(max_seqlen_q) + attn::kPrefillBN - 1) / attn::kPrefillBN;
-    PrefillPlan pl = plan_prefill(work, slots, bm, head_dim, key_tiles);
+    PrefillPlan pl = plan_prefill(work, c.slots, bm, head_dim, key_tiles);
     if (pl.parts > 1 && (!workspace || workspace_bytes < pl.ws_bytes))
         pl = plan_prefill(work, 0, bm, head_dim, key_tiles);    // no room for the split: run items whole
 
@@ -238,10 +265,13 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (head_dim == 128)
-        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16>(p, pl.grid, s)
-                                        : launch_prefill<128, attn::Fp16>(p, pl.grid, s);
-    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16>(p, pl.grid, s)
-                                    : launch_prefill<72, attn::Fp16>(p, pl.grid, s);
+        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16, 4>(p, pl.grid, s)
+                                        : launch_prefill<128, attn::Fp16, 4>(p, pl.grid, s);
+    if (c.waves == 8)
+        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16, 8>(p, pl.grid, s)
+                                        : launch_prefill<72, attn::Fp16, 8>(p, pl.grid, s);
+    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16, 4>(p, pl.grid, s)
+                                    : launch_prefill<72, attn::Fp16, 4>(p, pl.grid, s);
 }
 
 int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,

@@ -5,8 +5,11 @@
 // Implementation) as a tiled online softmax: the full score matrix is never
 // formed.
 //
-// Work decomposition.  One workgroup of 4 waves owns a tile of BM = 128
-// query rows of one (sequence, head); each wave owns 32 of those rows.  The
+// Work decomposition.  One workgroup of WAVES waves owns a tile of BM = 32
+// WAVES query rows of one (sequence, head); each wave owns 32 of those rows.
+// WAVES is 4 (BM 128), or 8 (BM 256) for head_dim 72 when the work items fill
+// the device at least once: twice the rows then share each K/V tile in LDS,
+// halving the tile DMA per flop, the costliest part at that head_dim.  The
 // workgroup streams the sequence's keys and values in tiles of BN = 64 rows
 // through double-buffered LDS.  The tiles go from global memory straight
 // into LDS (buffer loads with the LDS destination bit).  head_dim 128 lays
@@ -71,7 +74,6 @@ template <> struct PrefillShape<128> {
     static constexpr int KPITCH = 128;  // unpadded rows; chunks XOR-swizzled
     static constexpr int VPITCH = 128;
     static constexpr int ONES_COL = -1;
-    static constexpr int WAVES = 4;   // 8 measured slower: its waves move in lockstep
 };
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
@@ -80,14 +82,14 @@ template <> struct PrefillShape<72> {
     static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
-    static constexpr int WAVES = 4;
 };
 
 constexpr int kPrefillBN = 64;
 // Workgroup size: WAVES waves of 32 query rows each (BM = 32 WAVES rows).
-template <int D> constexpr int prefill_waves() { return PrefillShape<D>::WAVES; }
-template <int D> constexpr int prefill_bm() { return 32 * prefill_waves<D>(); }
-template <int D> constexpr int prefill_threads() { return 64 * prefill_waves<D>(); }
+// head_dim 128 runs 4 waves (8 measured level: the two waves of a SIMD then
+// belong to one workgroup and move in lockstep); head_dim 72 runs 4 or 8.
+constexpr int prefill_bm(int waves) { return 32 * waves; }
+constexpr int prefill_threads(int waves) { return 64 * waves; }
 
 // Rescaling threshold (log2 units) of the lazy online softmax: the running
 // max is raised, and O, l rescaled, only when some row's new max exceeds it by
@@ -97,16 +99,15 @@ constexpr float kRescaleThreshold = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, typename T>
-__global__ __launch_bounds__(prefill_threads<D>()) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, typename T, int WAVES>
+__global__ __launch_bounds__(prefill_threads(WAVES)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_fwd_kernel(PrefillParams p)
 {
-    constexpr int kPrefillThreads = prefill_threads<D>();
-    constexpr int WAVES = prefill_waves<D>();
+    constexpr int kPrefillThreads = prefill_threads(WAVES);
     using S = PrefillShape<D>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    constexpr int BM = prefill_bm<D>(), BN = kPrefillBN;
+    constexpr int BM = prefill_bm(WAVES), BN = kPrefillBN;
     constexpr int KP = S::KPITCH, VP = S::VPITCH;
     constexpr int CH = D / 8;                      // 16-byte chunks per row
 
@@ -218,7 +219,7 @@ void prefill_fwd_kernel(PrefillParams p)
     // wave w fills LDS rows RW w + 4 j .. +3, RW = 64 / WAVES.  Row R keeps
     // logical chunk c at position c ^ (R % 16) for K and c ^ 4 (R % 4) for V.
     // head_dim 72: the padded tile (KP or VP elements a row) is BN KP / 512
-    // instructions; instruction n = 4 j + w covers the 16-byte slots
+    // instructions; instruction n = WAVES j + w covers the 16-byte slots
     // 64 n .. 64 n + 63 of the tile, slot s being chunk s % (pitch / 8) of
     // row s / (pitch / 8); lanes on the pad chunks (>= 9) are masked off,
     // so the constant pad columns set up below stay as they are.
@@ -246,13 +247,13 @@ void prefill_fwd_kernel(PrefillParams p)
         constexpr int KC = KP / 8, VC = VP / 8;   // 16-byte slots per padded row
 #pragma unroll
         for (int j = 0; j < DJK; ++j) {
-            const int s = 64 * (4 * j + wave) + lane;
+            const int s = 64 * (WAVES * j + wave) + lane;
             dk_off[j] = static_cast<uint32_t>(s / KC) * row_bytes + 16u * static_cast<uint32_t>(s % KC);
             dk_act[j] = s % KC < CH;
         }
 #pragma unroll
         for (int j = 0; j < DJV; ++j) {
-            const int s = 64 * (4 * j + wave) + lane;
+            const int s = 64 * (WAVES * j + wave) + lane;
             dvp_off[j] = static_cast<uint32_t>(s / VC) * row_bytes + 16u * static_cast<uint32_t>(s % VC);
             dv_act[j] = s % VC < CH;
         }
@@ -264,7 +265,7 @@ void prefill_fwd_kernel(PrefillParams p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
         } else {
-            const int n = 4 * j + wave_s;
+            const int n = WAVES * j + wave_s;
             if (n < NKI && dk_act[j])
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(kbuf(par) + 512 * n), 16, dk_off[j],
                                                          0, 0, 0);
@@ -276,7 +277,7 @@ void prefill_fwd_kernel(PrefillParams p)
                 r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
                 static_cast<int>(4 * j * row_bytes), 0, 0);
         } else {
-            const int n = 4 * j + wave_s;
+            const int n = WAVES * j + wave_s;
             if (n < NVI && dv_act[j])
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dvp_off[j],
                                                          0, 0, 0);

@@ -296,6 +296,34 @@ def test_split_last_wave_matches_whole_items(D):
     check(f64(split), f64(whole), f"split vs whole D={D}")
 
 
+def test_eight_wave_items_with_a_split_last_wave():
+    # head_dim 72, 33024 tokens x 2 heads: 258 work items of 256 query rows
+    # (8-wave workgroups, chosen when the items fill the device once) -- one
+    # full wave plus two items, which are split into key ranges and merged
+    from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+    S, H, D = 33024, 2, 72
+    inp = gen.prefill_inputs([S], H, D, seed=79)
+    assert attn_varlen_fwd_workspace_size(1, S, H, D) > 0
+    d = to_gpu(inp)
+    split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=S)
+    whole = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                            max_seqlen_q=S,
+                            workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([[0, 255, 256, S - 257, S - 256, S - 1], rng.integers(0, S, 40),
+                           rng.integers(S - 512, S, 16)])
+    heads = rng.integers(0, H, rows.size)
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
+    check(f64(split[idx]), ref, "8-wave split", ref_abs=ref_abs)
+    check(f64(whole[idx]), ref, "8-wave whole", ref_abs=ref_abs)
+    check(f64(split), f64(whole), "8-wave split vs whole")
+
+
 @pytest.mark.parametrize("D", [72, 128])
 def test_small_grid_splits_every_item(D):
     # 16 query tiles x 4 heads = 64 items, far fewer than the device holds:
