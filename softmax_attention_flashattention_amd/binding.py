@@ -76,11 +76,13 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype=None, ndim=None):
+def _need(t, name, dtype=None, ndim=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -114,10 +116,10 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
     """
     fp16 = (torch.bfloat16, torch.float16)
     _need(q, "q", fp16, 3)
-    _need(k, "k", q.dtype, 3)
-    _need(v, "v", q.dtype, 3)
-    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
-    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    _need(k, "k", q.dtype, 3, device=q.device)
+    _need(v, "v", q.dtype, 3, device=q.device)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, device=q.device)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, device=q.device)
     total_q, H, D = q.shape
     if k.shape[1:] != (H, D) or v.shape != k.shape:
         raise ValueError("k and v must be [total_k, H, D] with q's H and D")
@@ -130,12 +132,14 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
     if out is None:
         out = torch.empty_like(q)
     else:
-        _need(out, "out", q.dtype, 3)
+        _need(out, "out", q.dtype, 3, device=q.device)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     if workspace is None:
         ws_bytes = attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, H, D)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    else:
+        _need(workspace, "workspace", device=q.device)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ws_ptr = _ptr(workspace) if ws_len else None
     rc = _load().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
@@ -177,10 +181,10 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
     """
     fp16 = (torch.bfloat16, torch.float16)
     _need(query, "query", fp16, 3)
-    _need(k_cache, "k_cache", query.dtype, 5)
-    _need(v_cache, "v_cache", query.dtype, 4)
-    _need(block_tables, "block_tables", torch.int32, 2)
-    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(k_cache, "k_cache", query.dtype, 5, device=query.device)
+    _need(v_cache, "v_cache", query.dtype, 4, device=query.device)
+    _need(block_tables, "block_tables", torch.int32, 2, device=query.device)
+    _need(seq_lens, "seq_lens", torch.int32, 1, device=query.device)
     num_seqs, num_query_heads, head_size = query.shape
     num_kv_heads = v_cache.shape[1]
     block_size = v_cache.shape[3]
@@ -197,13 +201,15 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", query.dtype, 3)
+        _need(out, "out", query.dtype, 3, device=query.device)
         if out.shape != query.shape:
             raise ValueError("out must have query's shape")
     ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, maxb,
                                                 block_size, partition_size)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
+    elif workspace is not None:
+        _need(workspace, "workspace", device=query.device)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = _load().attn_paged_decode(_ptr(query), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                    _ptr(seq_lens), num_seqs, num_query_heads, num_kv_heads,
@@ -227,10 +233,10 @@ def attn_chunk_delta_out(q, k, v, h, g, chunk_size=64, scale=None, out=None):
     """
     fp16 = (torch.bfloat16, torch.float16)
     _need(q, "q", fp16, 4)
-    _need(k, "k", q.dtype, 4)
-    _need(v, "v", q.dtype, 4)
-    _need(h, "h", q.dtype, 5)
-    _need(g, "g", torch.float32, 3)
+    _need(k, "k", q.dtype, 4, device=q.device)
+    _need(v, "v", q.dtype, 4, device=q.device)
+    _need(h, "h", q.dtype, 5, device=q.device)
+    _need(g, "g", torch.float32, 3, device=q.device)
     B, T, Hq, K = q.shape
     H, V = v.shape[2], v.shape[3]
     nc = (T + chunk_size - 1) // chunk_size
@@ -242,7 +248,7 @@ def attn_chunk_delta_out(q, k, v, h, g, chunk_size=64, scale=None, out=None):
     if out is None:
         out = torch.empty_like(v)
     else:
-        _need(out, "out", v.dtype, 4)
+        _need(out, "out", v.dtype, 4, device=q.device)
         if out.shape != v.shape:
             raise ValueError("out must have v's shape")
     rc = _load().attn_chunk_delta_out(_ptr(q), _ptr(k), _ptr(v), _ptr(h), _ptr(g), B, T, Hq, H, K,

@@ -176,6 +176,20 @@ def test_no_keys_gives_zero_rows(D):
     assert torch.count_nonzero(out).item() == 0
 
 
+def test_binding_rejects_host_buffers():
+    # every tensor handed to the library must be GPU memory of q's device
+    inp = gen.prefill_inputs([20], 2, 128, seed=43)
+    d = to_gpu(inp)
+    args = (d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"])
+    with pytest.raises(ValueError):
+        attn_varlen_fwd(*args, max_seqlen_q=20, workspace=torch.empty(16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        attn_varlen_fwd(*args, max_seqlen_q=20, out=torch.empty_like(inp["q"]))
+    with pytest.raises(ValueError):
+        attn_varlen_fwd(d["q"], inp["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                        max_seqlen_q=20)
+
+
 def test_runs_are_bitwise_deterministic():
     inp = gen.prefill_inputs([777], 4, 128, seed=41)
     a = run(inp).cpu()
