@@ -339,6 +339,23 @@ def test_eight_wave_items_with_a_split_last_wave():
 
 
 @pytest.mark.parametrize("D", [72, 128])
+def test_fp16_on_a_device_filling_grid(D):
+    # 8136 tokens x 16 heads in fp16: at head_dim 72 this grid takes the
+    # 8-wave workgroups, at 128 the 4-wave ones with a split last wave
+    S, H = 8136, 16
+    inp = gen.prefill_inputs([S], H, D, seed=81, dtype="fp16")
+    out = run(inp)
+    rng = np.random.default_rng(9)
+    rows = np.concatenate([[0, S - 1, (S // 256) * 256, (S // 128) * 128], rng.integers(0, S, 60)])
+    heads = rng.integers(0, H, rows.size)
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
+    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
+    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
+    check(got, ref, f"fp16 {S}x{H} D={D}", ref_abs=ref_abs)
+
+
+@pytest.mark.parametrize("D", [72, 128])
 def test_small_grid_splits_every_item(D):
     # 16 query tiles x 4 heads = 64 items, far fewer than the device holds:
     # every item is split into key ranges and merged
