@@ -310,7 +310,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (the shader clock settles over the first few launches)")
     ap.add_argument("--rotate", type=int, default=8,
                     help="decode input copies cycled through (8 x 138 MB > 256 MB cache)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
