@@ -80,15 +80,16 @@ typedef enum attn_dtype {
  *  num_heads      num_heads * head_dim < 2^25 (a key tile of 64 rows is
  *                 addressed with 32-bit byte offsets); larger returns
  *                 ATTN_ERR_INVALID_ARG
- *  scale          finite; the pages use head_dim^-1/2
+ *  scale          finite, of either sign or 0; the pages use head_dim^-1/2
  *  workspace      optional device memory, 256-byte aligned, of
  *                 attn_varlen_fwd_workspace_size(...) bytes.  When the work
- *                 items would leave the device's last wave of workgroups at
- *                 most half full, those items are split into key ranges
- *                 (when there are fewer items than half the device holds at
- *                 once, every item is) whose partial results go here and a
- *                 second kernel merges them.  NULL (or too small) runs every
- *                 item whole: the same result, only slower in that case.
+ *                 items would leave the device's last wave of workgroups
+ *                 partly empty, the items of that wave may be split into key
+ *                 ranges (when there are fewer items than half the device
+ *                 holds at once, every item is) whose partial results go
+ *                 here and a second kernel merges them.  NULL (or too small)
+ *                 runs every item whole: the same result up to rounding,
+ *                 only slower in those cases.
  *  out            [total_q, num_heads, head_dim], dtype.  Only rows inside a
  *                 query segment are written; a sequence with query rows but
  *                 no key rows gets all-zero rows.  Other rows are untouched.
