@@ -389,13 +389,13 @@ void prefill_fwd_kernel(PrefillParams p)
     auto max_finish = [&](float mx, bool valid) {
         mx = max_halves(mx);
         const float cand = mx * c;
-        const float m_new = valid && cand > m_run + kRescaleThreshold ? cand : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
-        const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
-        m_run = m_new;
-        l_run0 *= alpha;
-        l_run1 *= alpha;
-        if (rescale) {
+        const bool up = valid && cand > m_run + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform; rare after the first tile
+            const float m_new = up ? cand : m_run;
+            const float alpha = fast_exp2(m_run - m_new);   // 1 in the lanes that keep m
+            m_run = m_new;
+            l_run0 *= alpha;
+            l_run1 *= alpha;
 #pragma unroll
             for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
