@@ -342,6 +342,7 @@ void prefill_fwd_kernel(PrefillParams p)
     };
 
     float m_run = -INFINITY;   // running max of c*s for this lane's query (log2 domain)
+    float m_lim = -INFINITY;   // raw scores above this may need the running max raised
     float l_run0 = 0.f, l_run1 = 0.f;   // this lane's partial row sums (two chains)
     f32x16 oacc[S::DBLK];
 #pragma unroll
@@ -387,13 +388,19 @@ void prefill_fwd_kernel(PrefillParams p)
         return mx;
     };
     auto max_finish = [&](float mx, bool valid) {
-        mx = max_halves(mx);
-        const float cand = mx * c;
-        const bool up = valid && cand > m_run + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform; rare after the first tile
+        // a cheap, conservative test of this lane's half row against the
+        // raw-score limit first; the exact test below decides
+        if (valid && __builtin_amdgcn_ballot_w64(mx > m_lim) != 0) {   // wave-uniform; rare after the first tile
+            mx = max_halves(mx);
+            const float cand = mx * c;
+            const bool up = cand > m_run + kRescaleThreshold;
             const float m_new = up ? cand : m_run;
             const float alpha = fast_exp2(m_run - m_new);   // 1 in the lanes that keep m
             m_run = m_new;
+            // (m_run + threshold) / c, lowered by a relative 2^-16 so that no
+            // score the exact test would take fails the cheap one
+            const float lim = (m_run + kRescaleThreshold) / c;
+            m_lim = lim - fabsf(lim) * 0x1p-16f;
             l_run0 *= alpha;
             l_run1 *= alpha;
 #pragma unroll
