@@ -50,6 +50,17 @@ def test_prefill_split_and_merge_replays(D):
         f"prefill 2024 x 4 heads, D={D}")
 
 
+def test_prefill_eight_wave_split_replays():
+    # head_dim 72 on a device-filling grid: 8-wave workgroups, with the two
+    # items past the first full wave split into key ranges and merged
+    inp = gen.prefill_inputs([33024], 2, 72, seed=95)
+    d = to_gpu(inp)
+    replay_matches_eager(
+        lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                max_seqlen_q=33024),
+        "prefill 33024 x 2 heads, D=72, 8 waves")
+
+
 def test_prefill_varlen_batch_replays():
     inp = gen.prefill_inputs([300, 1, 777], 2, 128, seed=93)
     d = to_gpu(inp)
