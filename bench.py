@@ -489,6 +489,7 @@ def main():
             "kernel": f"prefill_fwd_kernel<{int(p_host['q'].shape[2])}, bf16>",
             "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
             "min_launch_ms": round(pre_ms[0], 4),
+            "median_launch_ms": round(pre_ms[len(pre_ms) // 2], 4),
         },
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
