@@ -97,15 +97,21 @@ int oracle_decode_bits_f64(const uint16_t *bits, int64_t n, int dtype, double *o
 /*
  * qrow[D], K[n][D], V[n][D] in double.  Writes out[D]; if lse is non-NULL it
  * receives log(sum_j exp(s_j)), and if wsum is non-NULL the sum of the
- * normalised softmax weights.  s is caller scratch of n doubles.
- * n == 0 gives an all-zero row, lse = -inf and wsum = 0.
+ * normalised softmax weights.  If out_abs is non-NULL it receives the same
+ * weights applied to |V| (sum_j w_j |v_j|, term for term what out would be
+ * for |V|): the magnitude that rounding errors of a weighted sum scale with.
+ * s is caller scratch of n doubles.  n == 0 gives an all-zero row (and
+ * out_abs), lse = -inf and wsum = 0.
  */
 static void attend_row(const double *qrow, const double *K, const double *V,
                        int64_t n, int D, double scale, double *s, double *out,
-                       double *lse, double *wsum)
+                       double *lse, double *wsum, double *out_abs)
 {
     for (int d = 0; d < D; ++d)
         out[d] = 0.0;
+    if (out_abs)
+        for (int d = 0; d < D; ++d)
+            out_abs[d] = 0.0;
     if (n == 0) {
         if (lse) *lse = -INFINITY;
         if (wsum) *wsum = 0.0;
@@ -128,9 +134,15 @@ static void attend_row(const double *qrow, const double *K, const double *V,
         z += e;
         for (int d = 0; d < D; ++d)
             out[d] += e * V[j * D + d];
+        if (out_abs)
+            for (int d = 0; d < D; ++d)
+                out_abs[d] += e * fabs(V[j * D + d]);
     }
     for (int d = 0; d < D; ++d)
         out[d] /= z;
+    if (out_abs)
+        for (int d = 0; d < D; ++d)
+            out_abs[d] /= z;
     if (lse) *lse = m + log(z);
     if (wsum) {
         double w = 0.0;
@@ -163,13 +175,14 @@ static void gather_rows(const uint16_t *x, int dtype, int64_t a, int64_t b,
  * Full varlen prefill.  q [total_q, H, D], k and v [total_k, H, D] (16-bit
  * bit patterns), cu_q and cu_k [num_seqs + 1].  out [total_q, H, D] double;
  * rows outside every query segment are set to NaN.  lse (optional,
- * [total_q, H]) and wsum (optional, [total_q, H]) as in attend_row.
+ * [total_q, H]), wsum (optional, [total_q, H]) and out_abs (optional,
+ * [total_q, H, D]) as in attend_row.
  */
 int oracle_varlen_fwd_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           int dtype, const int32_t *cu_q, const int32_t *cu_k,
                           int num_seqs, int64_t total_q, int64_t total_k,
                           int H, int D, double scale,
-                          double *out, double *lse, double *wsum)
+                          double *out, double *lse, double *wsum, double *out_abs)
 {
     if (num_seqs < 0 || H <= 0 || D <= 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_FP16))
         return -1;
@@ -177,6 +190,7 @@ int oracle_varlen_fwd_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
     if (cu_q[num_seqs] > total_q || cu_k[num_seqs] > total_k) return -3;
 
     for (int64_t i = 0; i < total_q * H * (int64_t)D; ++i) out[i] = NAN;
+    if (out_abs) for (int64_t i = 0; i < total_q * H * (int64_t)D; ++i) out_abs[i] = NAN;
     if (lse) for (int64_t i = 0; i < total_q * H; ++i) lse[i] = NAN;
     if (wsum) for (int64_t i = 0; i < total_q * H; ++i) wsum[i] = NAN;
 
@@ -204,7 +218,8 @@ int oracle_varlen_fwd_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
                     attend_row(qrow, K, V, nk, D, scale, s,
                                out + (r * H + h) * (int64_t)D,
                                lse ? lse + r * H + h : NULL,
-                               wsum ? wsum + r * H + h : NULL);
+                               wsum ? wsum + r * H + h : NULL,
+                               out_abs ? out_abs + (r * H + h) * (int64_t)D : NULL);
                 }
                 free(qrow);
                 free(s);
@@ -219,14 +234,14 @@ int oracle_varlen_fwd_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
 /*
  * The same definition evaluated only at n chosen (row, head) pairs, for
  * inputs too large to evaluate whole.  rows[i] must lie inside some query
- * segment.  out [n, D] double; lse optional [n].
+ * segment.  out [n, D] double; lse optional [n]; out_abs optional [n, D].
  */
 int oracle_varlen_fwd_rows_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                int dtype, const int32_t *cu_q, const int32_t *cu_k,
                                int num_seqs, int64_t total_q, int64_t total_k,
                                int H, int D, double scale,
                                const int64_t *rows, const int32_t *heads, int64_t n,
-                               double *out, double *lse)
+                               double *out, double *lse, double *out_abs)
 {
     if (num_seqs <= 0 || H <= 0 || D <= 0 || n < 0 || (dtype != ORACLE_BF16 && dtype != ORACLE_FP16))
         return -1;
@@ -260,7 +275,7 @@ int oracle_varlen_fwd_rows_f64(const uint16_t *q, const uint16_t *k, const uint1
             for (int d = 0; d < D; ++d)
                 qrow[d] = elem(q, (r * H + h) * (int64_t)D + d, dtype);
             attend_row(qrow, K, V, nk, D, scale, s, out + i * D,
-                       lse ? lse + i : NULL, NULL);
+                       lse ? lse + i : NULL, NULL, out_abs ? out_abs + i * D : NULL);
         }
         free(K); free(V); free(qrow); free(s);
     }
@@ -348,7 +363,7 @@ int oracle_paged_decode_f64(const uint16_t *query, const uint16_t *k_cache,
                     qrow[d] = elem(query, ((int64_t)s * num_query_heads + hq) * D + d, dtype);
                 attend_row(qrow, K, V, L, D, scale, sc,
                            out + ((int64_t)s * num_query_heads + hq) * D,
-                           lse ? lse + (int64_t)s * num_query_heads + hq : NULL, NULL);
+                           lse ? lse + (int64_t)s * num_query_heads + hq : NULL, NULL, NULL);
             } else {
                 #pragma omp atomic write
                 failed = rc;

@@ -61,9 +61,10 @@ def _declare(lib):
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_decode_bits_f64.argtypes = [P, i64, i32, P]
-    lib.oracle_varlen_fwd_f64.argtypes = [P, P, P, i32, P, P, i32, i64, i64, i32, i32, f64, P, P, P]
+    lib.oracle_varlen_fwd_f64.argtypes = [P, P, P, i32, P, P, i32, i64, i64, i32, i32, f64, P, P, P,
+                                          P]
     lib.oracle_varlen_fwd_rows_f64.argtypes = [P, P, P, i32, P, P, i32, i64, i64, i32, i32, f64,
-                                               P, P, i64, P, P]
+                                               P, P, i64, P, P, P]
     lib.oracle_paged_gather_f64.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, i32,
                                             P, P, P]
     lib.oracle_paged_decode_f64.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
@@ -115,8 +116,14 @@ def decode_bits(x):
 
 
 def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, return_lse=False,
-               return_wsum=False):
-    """Whole varlen prefill; rows outside every query segment come back NaN."""
+               return_wsum=False, return_abs=False):
+    """Whole varlen prefill; rows outside every query segment come back NaN.
+
+    ``return_abs`` also returns the same softmax weights applied to |v|
+    (what ``varlen_fwd`` gives for ``v.abs()``, computed in the same pass):
+    the magnitude the parity bar scales rounding errors with.  Extra results
+    follow ``out`` in the order lse, wsum, abs.
+    """
     qb, code = _bits(q)
     kb, kcode = _bits(k)
     vb, vcode = _bits(v)
@@ -133,16 +140,22 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, scale=None, return_lse=False
     out = np.empty((total_q, H, D), dtype=np.float64)
     lse = np.empty((total_q, H), dtype=np.float64) if return_lse else None
     wsum = np.empty((total_q, H), dtype=np.float64) if return_wsum else None
+    oabs = np.empty((total_q, H, D), dtype=np.float64) if return_abs else None
     rc = load().oracle_varlen_fwd_f64(_p(qb), _p(kb), _p(vb), code, _p(cq), _p(ck), cq.size - 1,
-                                      total_q, total_k, H, D, scale, _p(out), _p(lse), _p(wsum))
+                                      total_q, total_k, H, D, scale, _p(out), _p(lse), _p(wsum),
+                                      _p(oabs))
     _check(rc, "varlen_fwd")
-    res = [out] + ([lse] if return_lse else []) + ([wsum] if return_wsum else [])
+    res = ([out] + ([lse] if return_lse else []) + ([wsum] if return_wsum else [])
+           + ([oabs] if return_abs else []))
     return res[0] if len(res) == 1 else tuple(res)
 
 
 def varlen_fwd_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, rows, heads, scale=None,
-                    return_lse=False):
-    """The prefill definition at chosen (row, head) pairs only: out [n, D]."""
+                    return_lse=False, return_abs=False):
+    """The prefill definition at chosen (row, head) pairs only: out [n, D].
+
+    ``return_abs`` as in ``varlen_fwd``; extra results follow ``out`` in the
+    order lse, abs."""
     qb, code = _bits(q)
     kb, _ = _bits(k)
     vb, _ = _bits(v)
@@ -155,11 +168,14 @@ def varlen_fwd_rows(q, k, v, cu_seqlens_q, cu_seqlens_k, rows, heads, scale=None
     scale = D ** -0.5 if scale is None else float(scale)
     out = np.empty((rows.size, D), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64) if return_lse else None
+    oabs = np.empty((rows.size, D), dtype=np.float64) if return_abs else None
     rc = load().oracle_varlen_fwd_rows_f64(_p(qb), _p(kb), _p(vb), code, _p(cq), _p(ck),
                                            cq.size - 1, total_q, kb.shape[0], H, D, scale,
-                                           _p(rows), _p(heads), rows.size, _p(out), _p(lse))
+                                           _p(rows), _p(heads), rows.size, _p(out), _p(lse),
+                                           _p(oabs))
     _check(rc, "varlen_fwd_rows")
-    return (out, lse) if return_lse else out
+    res = [out] + ([lse] if return_lse else []) + ([oabs] if return_abs else [])
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def _decode_dims(query, k_cache, v_cache, block_tables):

@@ -354,3 +354,28 @@ def test_large_scores_stay_finite():
     q, k, v = (inp[n].to(torch.float64).transpose(0, 1).unsqueeze(0) for n in ("q", "k", "v"))
     ref = F.scaled_dot_product_attention(q, k, v, scale=200.0).squeeze(0).transpose(0, 1).numpy()
     np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------- weights applied to |v| (bar 2) --
+
+def test_absolute_value_output_is_the_oracle_on_abs_v():
+    # the same softmax weights applied to |v|, from the same pass: equal, bit
+    # for bit, to a separate evaluation on v.abs() (the same operations in the
+    # same order); at least |out| (triangle inequality) and equal to out where
+    # every value is non-negative; the row-subset entry gives the same bits
+    inp = gen.prefill_inputs([30, 0, 25], 3, 16, seed=52, seq_lens_k=[12, 4, 40])
+    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+    out, oabs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], *args, return_abs=True)
+    sep = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), *args)
+    assert np.array_equal(oabs, sep, equal_nan=True)
+    m = ~np.isnan(out)
+    assert np.all(oabs[m] >= np.abs(out[m]))
+    assert np.any(oabs[m] > np.abs(out[m]) + 1e-3)
+    pos, pos_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), *args, return_abs=True)
+    assert np.array_equal(pos, pos_abs, equal_nan=True)
+    rows = np.array([0, 29, 30, 54, 17])
+    heads = np.array([0, 2, 1, 0, 2])
+    sub, sub_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args, rows, heads,
+                                          return_abs=True)
+    assert np.array_equal(sub, out[rows, heads])
+    assert np.array_equal(sub_abs, oabs[rows, heads])
