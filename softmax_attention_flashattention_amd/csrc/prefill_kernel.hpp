@@ -230,9 +230,11 @@ void prefill_fwd_kernel(PrefillParams p)
     constexpr int RW = 64 / WAVES;      // tile rows per wave (head_dim 128)
     // (fixed size: a local array sized by a template-dependent constant here
     // makes hipcc drop the kernel's host launch stub for head_dim 128)
+    // The whole byte offset of every lane goes in the VGPR offset: the
+    // buffer range check covers that offset only (not the scalar one), so
+    // this is what turns rows past the sequence's last key into zeros.
     uint32_t dk_off[4] = {0u, 0u, 0u, 0u};
-    uint32_t dv_off = 0u;
-    uint32_t dvp_off[4] = {0u, 0u, 0u, 0u};   // head_dim 72: V slot offsets
+    uint32_t dv_off[4] = {0u, 0u, 0u, 0u};
     bool dk_act[4] = {false, false, false, false}, dv_act[4] = {false, false, false, false};
     if constexpr (SWZ) {
         const int rsub = lane >> 4, pos = lane & 15;
@@ -241,8 +243,11 @@ void prefill_fwd_kernel(PrefillParams p)
             const int R = RW * wave + 4 * j + rsub;
             dk_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (R & 15));
         }
-        dv_off = static_cast<uint32_t>(RW * wave + rsub) * row_bytes +
-                 16u * static_cast<uint32_t>(pos ^ (4 * (rsub & 3)));
+#pragma unroll
+        for (int j = 0; j < DJV; ++j) {
+            const int R = RW * wave + 4 * j + rsub;
+            dv_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (4 * (R & 3)));
+        }
     } else {
         constexpr int KC = KP / 8, VC = VP / 8;   // 16-byte slots per padded row
 #pragma unroll
@@ -254,7 +259,7 @@ void prefill_fwd_kernel(PrefillParams p)
 #pragma unroll
         for (int j = 0; j < DJV; ++j) {
             const int s = 64 * (WAVES * j + wave) + lane;
-            dvp_off[j] = static_cast<uint32_t>(s / VC) * row_bytes + 16u * static_cast<uint32_t>(s % VC);
+            dv_off[j] = static_cast<uint32_t>(s / VC) * row_bytes + 16u * static_cast<uint32_t>(s % VC);
             dv_act[j] = s % VC < CH;
         }
     }
@@ -274,12 +279,11 @@ void prefill_fwd_kernel(PrefillParams p)
     auto dma_v = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
         if constexpr (SWZ) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off,
-                static_cast<int>(4 * j * row_bytes), 0, 0);
+                r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off[j], 0, 0, 0);
         } else {
             const int n = WAVES * j + wave_s;
             if (n < NVI && dv_act[j])
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dvp_off[j],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dv_off[j],
                                                          0, 0, 0);
         }
     };

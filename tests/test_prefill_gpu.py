@@ -2,9 +2,11 @@
 
 Operator: atrex-bench "attention_forward" (#001), Reference Implementation.
 Every case feeds the HIP library and the oracle the same seeded inputs and
-applies the bar of tests/parity.py elementwise.  Full-size workloads are
-checked on sampled (row, head) pairs the oracle evaluates one by one,
-including the first and last rows (the partial last query tile).
+applies the bar of tests/parity.py elementwise.  The full-size workloads run
+with their output filled with NaN first, so an unwritten row cannot pass:
+the 276- and 8136-token ones are compared on every element, the 16742- and
+65556-token ones on one row from every work item (plus one whole head of the
+16742-token one), after checking that every element was written.
 """
 import numpy as np
 import pytest
@@ -28,11 +30,9 @@ def run(inp, out=None):
 
 
 def refs(inp):
-    """Oracle output and the oracle on |v| (the scale of bar 2)."""
-    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"])
-    ref = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], *args)
-    ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), *args)
-    return ref, ref_abs
+    """Oracle output and the same weights applied to |v| (the scale of bar 2)."""
+    return oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"],
+                             inp["cu_seqlens_k"], return_abs=True)
 
 
 def full_check(inp, what, bar1=True):
@@ -197,31 +197,131 @@ def test_runs_are_bitwise_deterministic():
     assert torch.equal(a, b)
 
 
-def sampled_check(name, n_rows=48, seed=7):
-    inp = gen.workload_inputs(name)
-    S = inp["q"].shape[0]
-    H = inp["q"].shape[1]
-    print(f"[prefill] workload {name}", flush=True)
-    out = run(inp)
+def run_nan_filled(inp):
+    """The call with `out` filled with NaN first, so a row no work item
+    writes stays NaN and fails the finiteness checks."""
+    d = to_gpu(inp)
+    out = torch.full_like(d["q"], float("nan"))
+    attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=inp["max_seqlen_q"], out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_at(inp, rows, heads):
+    """Oracle output and |v|-weighted magnitude at (row, head) pairs of a
+    single-sequence input, evaluated head by head: each head's chosen query
+    rows form one query segment against all of the sequence's keys, which is
+    the definition for those rows (query and key lengths may differ)."""
+    assert inp["cu_seqlens_q"].numel() == 2, "single-sequence inputs only"
+    rows, heads = np.asarray(rows, dtype=np.int64), np.asarray(heads, dtype=np.int64)
+    D = inp["q"].shape[2]
+    ref = np.empty((rows.size, D))
+    ref_abs = np.empty((rows.size, D))
+    for h in np.unique(heads):
+        sel = np.nonzero(heads == h)[0]
+        r = torch.from_numpy(rows[sel])
+        q = inp["q"][r, h:h + 1].contiguous()
+        k = inp["k"][:, h:h + 1].contiguous()
+        v = inp["v"][:, h:h + 1].contiguous()
+        cu_q = torch.tensor([0, sel.size], dtype=torch.int32)
+        o, a = oracle.varlen_fwd(q, k, v, cu_q, inp["cu_seqlens_k"], return_abs=True)
+        ref[sel], ref_abs[sel] = o[:, 0], a[:, 0]
+    return ref, ref_abs
+
+
+def rows_of_every_tile(S, H, tile, seed, extra_last=True):
+    """One seeded random query row from every (head, tile of `tile` rows),
+    plus the first and last rows of the last, partial tile of every head."""
     rng = np.random.default_rng(seed)
-    rows = np.concatenate([[0, S - 1, S - 2, (S // 128) * 128], rng.integers(0, S, n_rows)])
-    rows = np.clip(rows, 0, S - 1)
-    heads = rng.integers(0, H, rows.size)
-    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
-    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
-    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
+    nt = (S + tile - 1) // tile
+    rows, heads = [], []
+    for h in range(H):
+        for t in range(nt):
+            rows.append(int(rng.integers(t * tile, min(S, (t + 1) * tile))))
+            heads.append(h)
+        if extra_last:
+            rows += [(nt - 1) * tile, S - 1]
+            heads += [h, h]
+    return np.array(rows), np.array(heads)
+
+
+def every_item_check(name, tile, seed):
+    inp = gen.workload_inputs(name)
+    S, H, _ = inp["q"].shape
+    print(f"[prefill] workload {name}: every work item", flush=True)
+    out = run_nan_filled(inp)
+    # every element lies inside the one segment: all must have been written
+    assert bool(torch.isfinite(out).all()), f"{name}: rows left unwritten or non-finite"
+    rows, heads = rows_of_every_tile(S, H, tile, seed)
+    ref, ref_abs = oracle_at(inp, rows, heads)
     got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
-    return check(got, ref, name, ref_abs=ref_abs)
+    check(got, ref, f"{name}: one row per {tile}-row tile", ref_abs=ref_abs)
+    return inp, out
 
 
 def test_workload_s276_h4_d72_full():
     full_check(gen.workload_inputs("prefill_s276_h4_d72"), "prefill_s276_h4_d72")
 
 
-@pytest.mark.parametrize("name", ["prefill_s8136_h16_d72", "prefill_s16742_h32_d128",
-                                  "prefill_s65556_h16_d72"])
-def test_workload_sampled_rows(name):
-    sampled_check(name)
+def test_workload_s8136_h16_d72_every_element():
+    # 16 heads x 8136 rows at head_dim 72 (the 8-wave workgroups), every
+    # output element against the oracle
+    name = "prefill_s8136_h16_d72"
+    inp = gen.workload_inputs(name)
+    print(f"[prefill] workload {name}: every element", flush=True)
+    out = run_nan_filled(inp)
+    ref, ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"],
+                                     inp["cu_seqlens_k"], return_abs=True)
+    check(f64(out), ref, name, ref_abs=ref_abs)
+
+
+def test_workload_s16742_h32_d128_every_work_item():
+    # 131 query tiles x 32 heads = 4192 work items of 128 rows on 512
+    # resident workgroups: 8 full waves, and the last 96 items (head 31,
+    # query tiles 35..130) run as key ranges merged by log-sum-exp.  One row
+    # from every item, the first and last row of every split item, and all
+    # of head 31 (whole and split items) in full.
+    name = "prefill_s16742_h32_d128"
+    inp, out = every_item_check(name, 128, seed=12)
+    S = inp["q"].shape[0]
+    split_rows = np.concatenate([[t * 128, min(S, t * 128 + 128) - 1] for t in range(35, 131)])
+    ref, ref_abs = oracle_at(inp, split_rows, np.full(split_rows.size, 31))
+    got = f64(out[torch.from_numpy(split_rows).cuda(), 31])
+    check(got, ref, f"{name}: split items, first and last rows", ref_abs=ref_abs)
+    ref, ref_abs = oracle_at(inp, np.arange(S), np.full(S, 31))
+    check(f64(out[:, 31]), ref, f"{name}: head 31 in full", ref_abs=ref_abs)
+
+
+def test_workload_s65556_h16_d72_every_work_item():
+    # 257 tiles of 256 rows x 16 heads = 4112 items on the 8-wave path (256
+    # resident workgroups): 16 full waves, and the last 16 items (head 15)
+    # split into key ranges.  One row from every 128-row half of every item.
+    every_item_check("prefill_s65556_h16_d72", 128, seed=13)
+
+
+@pytest.mark.parametrize("D", [72, 128])
+@pytest.mark.parametrize("Sk", [1, 17, 38, 300])
+def test_keys_past_the_last_segment_are_never_read(D, Sk):
+    # k and v are the leading rows of buffers whose further rows hold NaN: a
+    # tile load that reached past the last key would pull NaN into the
+    # product (0 weight times NaN is NaN).  Key lengths leave a partial last
+    # key tile and a partial 4-row DMA group; a second sequence ends there.
+    H = 3
+    for lens_q, lens_k in (([50], [Sk]), ([20, 33], [64, Sk])):
+        inp = gen.prefill_inputs(lens_q, H, D, seed=90 + Sk, seq_lens_k=lens_k)
+        tk = inp["k"].shape[0]
+        d = to_gpu(inp)
+        kb = torch.full((tk + 80, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        vb = torch.full((tk + 80, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        kb[:tk] = d["k"]
+        vb[:tk] = d["v"]
+        out = torch.full_like(d["q"], float("nan"))
+        attn_varlen_fwd(d["q"], kb[:tk], vb[:tk], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                        max_seqlen_q=inp["max_seqlen_q"], out=out)
+        torch.cuda.synchronize()
+        ref, ref_abs = refs(inp)
+        check(f64(out), ref, f"NaN past the keys D={D} Sk={Sk} {lens_k}", ref_abs=ref_abs)
 
 
 def test_many_sequences_of_random_lengths():
@@ -262,25 +362,6 @@ def test_varlen_batch_with_split_tail():
     idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
     check(f64(split[idx]), ref, "varlen split", ref_abs=ref_abs)
     check(f64(split), f64(whole), "varlen split vs whole")
-
-
-def test_workload_s16742_split_items_sampled():
-    # the benchmark's launch: 131 query tiles x 32 heads = 4192 items on 512
-    # resident workgroups, so the last 96 items (head 31, query rows from
-    # 35 * 128 on) run as key ranges merged by log-sum-exp; sample them
-    name = "prefill_s16742_h32_d128"
-    inp = gen.workload_inputs(name)
-    print(f"[prefill] {name} split items", flush=True)
-    out = run(inp)
-    S = inp["q"].shape[0]
-    rng = np.random.default_rng(11)
-    rows = np.concatenate([[35 * 128, 35 * 128 + 127, S - 1], rng.integers(35 * 128, S, 61)])
-    heads = np.full(rows.size, 31)
-    args = (inp["cu_seqlens_q"], inp["cu_seqlens_k"], rows, heads)
-    ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
-    ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
-    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
-    check(got, ref, f"{name} split items", ref_abs=ref_abs)
 
 
 @pytest.mark.parametrize("D", [72, 128])
