@@ -17,7 +17,7 @@
  *  - Every tensor pointer is device memory owned by the caller.  The library
  *    never allocates, frees or synchronises; it writes only `out` and the
  *    caller's `workspace` (prefill's key-range split, decode's context
- *    partitions).
+ *    partitions), or for attn_paged_decode_noalloc its static buffer.
  *  - Calls enqueue their kernels on `stream` (a hipStream_t; NULL is the null
  *    stream) and return at once.  They never read device memory on the host
  *    and issue no memset, so a call can be captured into a HIP graph and
@@ -33,8 +33,10 @@
  *    caller error with unspecified output values; the kernels clamp such
  *    indices so that they never read or write outside the buffers described
  *    by the size arguments.
- *  - The library keeps no mutable global state; calls on different streams
- *    may run concurrently as long as their `out`/`workspace` buffers differ.
+ *  - The only mutable global state is attn_paged_decode_noalloc's device
+ *    buffer (one per GPU) and its looked-up address; other calls on different
+ *    streams may run concurrently as long as their `out`/`workspace` buffers
+ *    differ.
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H
@@ -151,6 +153,37 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
                       int64_t num_blocks, float scale, int32_t dtype,
                       int32_t partition_size, void *workspace, size_t workspace_bytes,
                       void *out, void *stream);
+
+/*
+ * attn_paged_decode_noalloc -- attn_paged_decode without a caller workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It
+ * allocates nothing.  Arguments, layouts, results and errors are those of
+ * attn_paged_decode; a split context keeps its per-partition partial results
+ * in a static device buffer of ATTN_NOALLOC_SCRATCH_BYTES instead (one per
+ * GPU, held until the process ends).
+ *
+ *  - Returns ATTN_ERR_WORKSPACE, before touching the device, when
+ *    attn_paged_decode_workspace_size(...) for the call exceeds
+ *    ATTN_NOALLOC_SCRATCH_BYTES (pick a larger partition_size, or use
+ *    attn_paged_decode with a workspace).
+ *  - The first call on a device looks the buffer's address up (a runtime
+ *    symbol query, no allocation); make it outside graph capture if the
+ *    capture mode forbids runtime queries.  `stream` must belong to the
+ *    current device.
+ *  - Every call on one GPU shares that GPU's buffer: calls that may overlap
+ *    on one GPU (different streams, different host threads) race and give
+ *    unspecified output.  Calls in one stream are ordered and safe.  Nothing
+ *    in the buffer needs to start zeroed: each partition a merge reads is
+ *    written by the same call.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens,
+                              int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t dtype,
+                              int32_t partition_size, void *out, void *stream);
 
 /*
  * Number of context partitions attn_paged_decode will use for these sizes

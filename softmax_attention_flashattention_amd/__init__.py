@@ -6,9 +6,10 @@ they only marshal arguments (shapes, pointers, the current HIP stream) and
 call the HIP library.  Nothing is computed here.
 """
 from .binding import (attn_varlen_fwd, attn_varlen_fwd_workspace_size, attn_paged_decode,
-                      attn_paged_decode_workspace_size, attn_paged_decode_num_partitions,
-                      attn_chunk_delta_out, attn_status_string, AttnError, library_path)
+                      attn_paged_decode_noalloc, attn_paged_decode_workspace_size,
+                      attn_paged_decode_num_partitions, attn_chunk_delta_out, attn_status_string,
+                      AttnError, library_path)
 
 __all__ = ["attn_varlen_fwd", "attn_varlen_fwd_workspace_size", "attn_paged_decode",
-           "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions",
+           "attn_paged_decode_noalloc", "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions",
            "attn_chunk_delta_out", "attn_status_string", "AttnError", "library_path"]

@@ -55,6 +55,9 @@ def _load():
     lib.attn_paged_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32, i32,
                                       i32, P, sz, P, P]
     lib.attn_paged_decode.restype = ctypes.c_int
+    lib.attn_paged_decode_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
+                                              i32, i32, P, P]
+    lib.attn_paged_decode_noalloc.restype = ctypes.c_int
     lib.attn_paged_decode_num_partitions.argtypes = [i32, i32, i32]
     lib.attn_paged_decode_num_partitions.restype = i32
     lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -168,17 +171,9 @@ def attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, max_b
                                                     int(block_size), int(partition_size))
 
 
-def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=None, out=None,
-                      partition_size=0, workspace=None):
-    """Paged single-query decode with grouped-query heads (calls ``attn_paged_decode``).
-
-    query [num_seqs, Hq, D]; k_cache [num_blocks, Hkv, D/8, block_size, 8];
-    v_cache [num_blocks, Hkv, D, block_size]; block_tables int32
-    [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs].  ``scale``
-    defaults to D**-0.5.  ``partition_size`` (tokens, 0 = library default)
-    sets the split-K granularity; the workspace it needs is allocated here
-    unless one is passed.
-    """
+def _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out):
+    """Checks the decode tensors, derives the sizes from their shapes and
+    returns (sizes, scale, out)."""
     fp16 = (torch.bfloat16, torch.float16)
     _need(query, "query", fp16, 3)
     _need(k_cache, "k_cache", query.dtype, 5, device=query.device)
@@ -204,6 +199,23 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
         _need(out, "out", query.dtype, 3, device=query.device)
         if out.shape != query.shape:
             raise ValueError("out must have query's shape")
+    sizes = (num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks)
+    return sizes, scale, out
+
+
+def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=None, out=None,
+                      partition_size=0, workspace=None):
+    """Paged single-query decode with grouped-query heads (calls ``attn_paged_decode``).
+
+    query [num_seqs, Hq, D]; k_cache [num_blocks, Hkv, D/8, block_size, 8];
+    v_cache [num_blocks, Hkv, D, block_size]; block_tables int32
+    [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs].  ``scale``
+    defaults to D**-0.5.  ``partition_size`` (tokens, 0 = library default)
+    sets the split-K granularity; the workspace it needs is allocated here
+    unless one is passed.
+    """
+    sizes, scale, out = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out)
+    num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
     ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, maxb,
                                                 block_size, partition_size)
     if workspace is None and ws_bytes > 0:
@@ -218,6 +230,28 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
                                    ws_len, _ptr(out), _stream(query.device))
     if rc != 0:
         raise AttnError("attn_paged_decode", rc)
+    return out
+
+
+def attn_paged_decode_noalloc(query, k_cache, v_cache, block_tables, seq_lens, scale=None,
+                              out=None, partition_size=0):
+    """``attn_paged_decode`` without a workspace (calls ``attn_paged_decode_noalloc``).
+
+    The library keeps a split context's partial results in its own static
+    per-GPU buffer, so the call allocates nothing when ``out`` is passed;
+    calls that may overlap on one GPU race for that buffer.  Raises
+    AttnError(ATTN_ERR_WORKSPACE) when the split needs more than the buffer
+    holds.
+    """
+    sizes, scale, out = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out)
+    num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
+    rc = _load().attn_paged_decode_noalloc(_ptr(query), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(block_tables), _ptr(seq_lens), num_seqs,
+                                           num_query_heads, num_kv_heads, head_size, block_size,
+                                           maxb, num_blocks, scale, _DTYPE[query.dtype],
+                                           int(partition_size), _ptr(out), _stream(query.device))
+    if rc != 0:
+        raise AttnError("attn_paged_decode_noalloc", rc)
     return out
 
 

@@ -4,11 +4,20 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn.h"
 #include "chunk_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "prefill_kernel.hpp"
+
+// Device-side scratch of attn_paged_decode_noalloc: the per-partition
+// (max, sum) pairs and partial outputs of a split context, laid out as the
+// caller workspace of attn_paged_decode.  Every GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -184,6 +193,27 @@ int partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition
     return (max_blocks_per_seq + pb - 1) / pb;
 }
 
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`.
+int scratch_address(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return ATTN_ERR_HIP;
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,12 +322,16 @@ size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_head
     return ml + rows * static_cast<size_t>(head_size) * sizeof(float);
 }
 
-int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+}  // extern "C"
+
+namespace {
+
+// Argument checks of a paged-decode call, before anything touches the device.
+int check_decode_args(const void *query, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
                       int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                      int32_t dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                      void *out, void *stream)
+                      int32_t dtype, int32_t partition_size, const void *out)
 {
     if (num_seqs < 0 || num_query_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
         block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 || partition_size < 0)
@@ -316,7 +350,19 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
     if (!aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(block_tables, 4) || !aligned(seq_lens, 4))
         return ATTN_ERR_INVALID_ARG;
+    return ATTN_OK;
+}
 
+// The launches of a checked paged-decode call with a workspace of at least
+// attn_paged_decode_workspace_size bytes (or none, when that size is 0).
+int launch_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+                        const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                        int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
+                        int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                        float scale, int32_t dtype, int32_t partition_size, void *workspace,
+                        size_t workspace_bytes, void *out, void *stream)
+{
+    const int G = num_query_heads / num_kv_heads;
     int part_blocks = 1;
     const int np = partitions(max_blocks_per_seq, block_size, partition_size, &part_blocks);
     if (np < 1) return ATTN_ERR_INVALID_ARG;
@@ -355,6 +401,53 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, head_size, grid, s)
                                     : dispatch_decode<attn::Fp16>(p, head_size, grid, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
+                      int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                      int32_t dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *out, void *stream)
+{
+    const int rc = check_decode_args(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                     num_query_heads, num_kv_heads, head_size, block_size,
+                                     max_blocks_per_seq, num_blocks, scale, dtype, partition_size, out);
+    if (rc != ATTN_OK || num_seqs == 0) return rc;
+    return launch_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                               num_query_heads, num_kv_heads, head_size, block_size,
+                               max_blocks_per_seq, num_blocks, scale, dtype, partition_size,
+                               workspace, workspace_bytes, out, stream);
+}
+
+int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens,
+                              int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t dtype,
+                              int32_t partition_size, void *out, void *stream)
+{
+    const int rc = check_decode_args(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                     num_query_heads, num_kv_heads, head_size, block_size,
+                                     max_blocks_per_seq, num_blocks, scale, dtype, partition_size, out);
+    if (rc != ATTN_OK) return rc;
+    const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size,
+                                                         max_blocks_per_seq, block_size, partition_size);
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    // set-up on the first call on a device (also when no split needs it)
+    void *ws = nullptr;
+    const int src = scratch_address(&ws);
+    if (src != ATTN_OK) return src;
+    if (num_seqs == 0) return ATTN_OK;
+    return launch_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                               num_query_heads, num_kv_heads, head_size, block_size,
+                               max_blocks_per_seq, num_blocks, scale, dtype, partition_size,
+                               need > 0 ? ws : nullptr, need > 0 ? ATTN_NOALLOC_SCRATCH_BYTES : 0,
+                               out, stream);
 }
 
 int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h, const float *g,

@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) >= {"attn_varlen_fwd", "attn_varlen_fwd_workspace_size",
                           "attn_paged_decode", "attn_status_string",
                           "attn_paged_decode_workspace_size", "attn_paged_decode_num_partitions",
-                          "attn_chunk_delta_out"}
+                          "attn_chunk_delta_out", "attn_paged_decode_noalloc"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
 
@@ -128,6 +128,32 @@ def test_decode_workspace_rules(lib):
     assert decode(lib, maxb=64, ws=None, ws_bytes=0) == WORKSPACE
     assert decode(lib, maxb=64, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
     assert decode(lib, maxb=64, ws=FAKE + 16, ws_bytes=need) == WORKSPACE   # not 256-aligned
+
+
+def decode_noalloc(lib, **kw):
+    a = dict(query=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, num_seqs=4, hq=16, hkv=16, d=128,
+             bs=16, maxb=4, nb=32, scale=0.1, dtype=0, part=0, out=FAKE)
+    a.update(kw)
+    return lib.attn_paged_decode_noalloc(a["query"], a["k"], a["v"], a["bt"], a["sl"],
+                                         a["num_seqs"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                         a["maxb"], a["nb"], a["scale"], a["dtype"], a["part"],
+                                         a["out"], None)
+
+
+def test_decode_noalloc_rejects_what_its_buffer_cannot_hold(lib):
+    # the same argument checks as attn_paged_decode, then the split's partial
+    # results must fit the static 64 MiB buffer: refused before any device call
+    assert decode_noalloc(lib, hkv=3) == INVALID
+    assert decode_noalloc(lib, d=64) == UNSUPPORTED
+    assert decode_noalloc(lib, part=24) == INVALID
+    assert decode_noalloc(lib, query=None) == INVALID
+    limit = 64 << 20
+    big = dict(num_seqs=256, hq=64, hkv=8, maxb=64, part=16)      # 64 partitions each
+    need = lib.attn_paged_decode_workspace_size(256, 64, 128, 64, 16, 16)
+    assert need > limit
+    assert decode_noalloc(lib, **big) == WORKSPACE
+    fits = lib.attn_paged_decode_workspace_size(256, 64, 128, 64, 16, 256)   # 4 partitions
+    assert 0 < fits <= limit
 
 
 def test_decode_empty_batch_is_ok_without_launch(lib):
