@@ -9,6 +9,7 @@
 #include "attn.h"
 #include "chunk_kernel.hpp"
 #include "decode_kernel.hpp"
+#include "prefill_d128_kernel.hpp"
 #include "prefill_kernel.hpp"
 
 // Device-side scratch of attn_paged_decode_noalloc: the per-partition
@@ -41,23 +42,43 @@ int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t strea
     return launch_status();
 }
 
+template <typename T>
+int launch_prefill_d128(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn::prefill_fwd_d128_kernel<T>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::kD128Threads), 0, stream, p);
+    int rc = launch_status();
+    if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
+    hipLaunchKernelGGL((attn::prefill_merge_kernel<128, attn::kD128BM, T>),
+                       dim3(static_cast<unsigned>((p.total_work - p.whole_work) *
+                                                  attn::merge_blocks<128, attn::kD128BM>())),
+                       dim3(attn::kMergeThreads), 0, stream, p);
+    return launch_status();
+}
+
 // Work items that fit the device at once: compute units x resident
-// workgroups per unit (0 when the runtime cannot tell, e.g. no device).
-template <int D, int W>
-int prefill_slots()
+// workgroups per unit of `kernel` (0 when the runtime cannot tell, e.g. no
+// device).
+template <typename K>
+int kernel_slots(K kernel, int threads)
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, attn::prefill_fwd_kernel<D, attn::Bf16, W>, attn::prefill_threads(W), 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
     return e == hipSuccess ? cus * per_cu : 0;
+}
+template <int D, int W>
+int prefill_slots()
+{
+    return kernel_slots(attn::prefill_fwd_kernel<D, attn::Bf16, W>, attn::prefill_threads(W));
 }
 
 // Waves per workgroup for a call, and the resulting work items and slots.
-// head_dim 72 takes 8 waves (256 query rows) when those items fill every
-// slot at least once; smaller grids keep 4 (the shorter Shapes rows ran up
-// to 30% slower with 8: fewer, longer work items).
+// head_dim 128 runs prefill_fwd_d128_kernel: 4 waves of 64 query rows (256
+// rows per item).  head_dim 72 takes 8 waves (256 query rows) when those
+// items fill every slot at least once; smaller grids keep 4 (the shorter
+// Shapes rows ran up to 30% slower with 8: fewer, longer work items).
 struct PrefillShapeChoice {
     int waves = 4, bm = 128, slots = 0;
     int64_t qtiles = 0, work = 0;
@@ -76,9 +97,9 @@ PrefillShapeChoice choose_prefill(int64_t num_seqs, int64_t max_seqlen_q, int64_
             c.slots = prefill_slots<72, 4>();
         }
     } else {
-        c.slots = prefill_slots<128, 4>();
+        c.slots = kernel_slots(attn::prefill_fwd_d128_kernel<attn::Bf16>, attn::kD128Threads);
     }
-    c.bm = attn::prefill_bm(c.waves);
+    c.bm = head_dim == 128 ? attn::kD128BM : attn::prefill_bm(c.waves);
     c.qtiles = (max_seqlen_q + c.bm - 1) / c.bm;
     c.work = num_seqs * num_heads * c.qtiles;
     return c;
@@ -295,8 +316,8 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     if (head_dim == 128)
-        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<128, attn::Bf16, 4>(p, pl.grid, s)
-                                        : launch_prefill<128, attn::Fp16, 4>(p, pl.grid, s);
+        return dtype == ATTN_DTYPE_BF16 ? launch_prefill_d128<attn::Bf16>(p, pl.grid, s)
+                                        : launch_prefill_d128<attn::Fp16>(p, pl.grid, s);
     if (c.waves == 8)
         return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16, 8>(p, pl.grid, s)
                                         : launch_prefill<72, attn::Fp16, 8>(p, pl.grid, s);

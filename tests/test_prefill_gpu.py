@@ -277,18 +277,19 @@ def test_workload_s8136_h16_d72_every_element():
 
 
 def test_workload_s16742_h32_d128_every_work_item():
-    # 131 query tiles x 32 heads = 4192 work items of 128 rows on 512
-    # resident workgroups: 8 full waves, and the last 96 items (head 31,
-    # query tiles 35..130) run as key ranges merged by log-sum-exp.  One row
-    # from every item, the first and last row of every split item, and all
-    # of head 31 (whole and split items) in full.
+    # 66 query tiles x 32 heads = 2112 work items of 256 rows on 512 resident
+    # workgroups: 4 full waves, and the last 64 items (head 31, query tiles
+    # 2..65) run as key ranges merged by log-sum-exp.  One row from every
+    # 128-row half of every item, the first and last row of every 128-row
+    # tile of head 31 (so of every item there, whole or split, whatever the
+    # item size), and all of head 31 in full.
     name = "prefill_s16742_h32_d128"
     inp, out = every_item_check(name, 128, seed=12)
     S = inp["q"].shape[0]
-    split_rows = np.concatenate([[t * 128, min(S, t * 128 + 128) - 1] for t in range(35, 131)])
+    split_rows = np.concatenate([[t * 128, min(S, t * 128 + 128) - 1] for t in range((S + 127) // 128)])
     ref, ref_abs = oracle_at(inp, split_rows, np.full(split_rows.size, 31))
     got = f64(out[torch.from_numpy(split_rows).cuda(), 31])
-    check(got, ref, f"{name}: split items, first and last rows", ref_abs=ref_abs)
+    check(got, ref, f"{name}: head 31, first and last rows of every tile", ref_abs=ref_abs)
     ref, ref_abs = oracle_at(inp, np.arange(S), np.full(S, 31))
     check(f64(out[:, 31]), ref, f"{name}: head 31 in full", ref_abs=ref_abs)
 
@@ -336,9 +337,9 @@ def test_many_sequences_of_random_lengths():
 
 
 def test_varlen_batch_with_split_tail():
-    # 3 sequences x 4 heads, up to 32 query tiles: 384 items fill more than
-    # half of the 512 resident workgroups, so every item is split into key
-    # ranges, each over its own sequence's keys
+    # 3 sequences x 4 heads, up to 16 query tiles of 256 rows: 192 items,
+    # under half of the 512 resident workgroups, so every item is split into
+    # key ranges, each over its own sequence's keys
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
     lens = [3000, 1500, 4096]
     inp = gen.prefill_inputs(lens, 4, 128, seed=62, seq_lens_k=[2500, 4100, 4096])
@@ -366,9 +367,10 @@ def test_varlen_batch_with_split_tail():
 
 @pytest.mark.parametrize("D", [72, 128])
 def test_split_last_wave_matches_whole_items(D):
-    # 516 heads x 1 query tile: one full wave of workgroups plus a few items,
-    # which the library splits into key ranges (5 key tiles over up to 8
-    # ranges, so some ranges are empty) and merges
+    # 516 heads x 300 rows: one or two full waves of workgroups (one query
+    # tile of 128 rows at head_dim 72, two of 256 at 128) plus a few items,
+    # which the library splits into key ranges (5 key tiles of 64 rows, 10
+    # of 32, over up to 8 ranges) and merges
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
     inp = gen.prefill_inputs([300], 516, D, seed=77)
     assert attn_varlen_fwd_workspace_size(1, 300, 516, D) > 0
@@ -422,7 +424,7 @@ def test_eight_wave_items_with_a_split_last_wave():
 @pytest.mark.parametrize("D", [72, 128])
 def test_fp16_on_a_device_filling_grid(D):
     # 8136 tokens x 16 heads in fp16: at head_dim 72 this grid takes the
-    # 8-wave workgroups, at 128 the 4-wave ones with a split last wave
+    # 8-wave workgroups, at 128 exactly one wave of 512 items of 256 rows
     S, H = 8136, 16
     inp = gen.prefill_inputs([S], H, D, seed=81, dtype="fp16")
     out = run(inp)
@@ -458,12 +460,13 @@ def test_small_grid_splits_every_item(D):
     check(f64(split), f64(whole), f"small grid split vs whole D={D}")
 
 
-@pytest.mark.parametrize("H", [26, 10])
+@pytest.mark.parametrize("H", [52, 20])
 def test_more_than_half_full_wave_is_split(H):
-    # 32 query tiles x H heads at 64 key tiles: with 512 resident workgroups,
-    # 26 heads leave 320 items for a second wave and 10 heads make one wave
-    # of 320; either tail is split into the number of key ranges that
-    # finishes it soonest (3 here) and merged
+    # 16 query tiles of 256 rows (head_dim 128) x H heads at 64 key tiles of
+    # 64 rows: with 512 resident workgroups, 52 heads leave 320 items for a
+    # second wave and 20 heads make one wave of 320; either tail is split
+    # into the number of key ranges that finishes it soonest (3 here) and
+    # merged
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
     S = 4096
     inp = gen.prefill_inputs([S], H, 128, seed=80 + H)
