@@ -15,10 +15,14 @@ back after the step loop (a lone 26-us call's event pair would also time its
 dispatch).
 
 Printed: one JSON line with prefill TFLOP/s (the headline value), decode
-GB/s, both against MI355X roofline peaks, the CPU oracle's rate on a bounded
-sample (rank 0, one GPU), and under "page_context" the pages' own T_SOL and
-T_Prod for the same workloads (hardware labelled only "XPU-A"; context, not a
-target) beside this run's per-launch times.  Only one GPU is used: --gpus above 1 exits
+GB/s, both against MI355X roofline peaks and with the shader clock sampled
+during the timed prefill launches; under "configs" the other prefill
+workloads of the configuration list, each timed on its own; the CPU oracle's
+rate on a bounded sample and its time on every workload (in full where that
+takes seconds, else a sample with the full time extrapolated, labelled); and
+under "page_context" the pages' own T_SOL and T_Prod for the same workloads
+(hardware labelled only "XPU-A"; context, not a target) beside this run's
+per-launch times.  Only one GPU is used: --gpus above 1 exits
 with a message.
 """
 import argparse
@@ -39,11 +43,76 @@ DECODE = "decode_b256_ctx64_h16_kv16_d128"
 CHUNK = "chunk_t14807_h32_hq16"
 # the sources each kernel's counter figures depend on
 KERNEL_SOURCES = {
+    "prefill_fwd_d128_kernel": ["prefill_d128_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "prefill_fwd_kernel": ["prefill_kernel.hpp", "device_common.hpp"],
     "decode_partition_kernel": ["decode_kernel.hpp", "device_common.hpp"],
     "chunk_delta_out_kernel": ["chunk_kernel.hpp", "device_common.hpp"],
 }
-ALL_SOURCES = ["prefill_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp", "device_common.hpp"]
+ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp",
+               "device_common.hpp"]
+# the page rows ("attention_forward" Shapes table) of the prefill workloads
+WORKLOAD_PAGE_ROWS = {"prefill_s276_h4_d72": 11, "prefill_s8136_h16_d72": 4,
+                      "prefill_s16742_h32_d128": 9, "prefill_s65556_h16_d72": 8}
+# the prefill workloads of the benchmark configuration list
+PREFILL_CONFIGS = ["prefill_s276_h4_d72", "prefill_s8136_h16_d72", "prefill_s16742_h32_d128",
+                   "prefill_s65556_h16_d72"]
+
+
+def prefill_kernel(head_dim):
+    """(name prefix, label) of the kernel that runs a prefill at this head_dim."""
+    if head_dim == 128:
+        return "prefill_fwd_d128_kernel", "prefill_fwd_d128_kernel<bf16>"
+    return "prefill_fwd_kernel", f"prefill_fwd_kernel<{head_dim}, bf16>"
+
+
+class ClockSampler:
+    """Samples the GPU shader clock (the current level of pp_dpm_sclk in sysfs)
+    from a background thread while a timed region runs."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for path in self.paths:
+            try:
+                with open(path) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            return float(re.search(r"(\d+)\s*[Mm]hz", line).group(1))
+            except (OSError, AttributeError, ValueError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.paths:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "pp_dpm_sclk", "samples": 0, "note": "not readable on this machine"}
+        v = sorted(self.samples)
+        return {"source": "sysfs pp_dpm_sclk (current level), sampled during the timed prefill launches",
+                "samples": len(v), "mean_mhz": round(sum(v) / len(v)), "median_mhz": v[len(v) // 2],
+                "min_mhz": v[0], "max_mhz": v[-1]}
 
 
 def kernel_source_hash(names):
@@ -120,6 +189,58 @@ def cpu_baseline(budget_s):
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} (query row, head) pairs of {PREFILL}, each against all {S} keys, "
                       f"float64, {t:.1f} s"}
+
+
+def oracle_per_config(budget_s):
+    """The oracle, as it stands, on each benchmark workload: in full where that
+    takes seconds (the 276-token prefill, the decode workload), else on the
+    first n query rows of head 0 (one query segment of n rows against all of
+    the sequence's keys: the definition for those rows, through the same
+    whole-workload entry point), with the full-workload time extrapolated as
+    seconds x (rows x heads) / n and labelled as such.  n is sized to about
+    budget_s seconds of CPU work."""
+    import oracle
+    import torch
+    from softmax_attention_flashattention_amd import inputs as gen
+    threads = oracle.num_threads()
+    res = {}
+    for name in PREFILL_CONFIGS:
+        inp = gen.workload_inputs(name)
+        S, H, D = inp["q"].shape
+        flops = prefill_flops(inp)
+        if S * S * H <= 1 << 24:
+            t0 = time.perf_counter()
+            oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"])
+            t = time.perf_counter() - t0
+            res[name] = {"mode": "full", "seconds": round(t, 4), "tflops": flops / t / 1e12}
+            continue
+        k, v = inp["k"][:, :1].contiguous(), inp["v"][:, :1].contiguous()
+
+        def run(n):
+            q = inp["q"][:n, :1].contiguous()
+            cu_q = torch.tensor([0, n], dtype=torch.int32)
+            t0 = time.perf_counter()
+            oracle.varlen_fwd(q, k, v, cu_q, inp["cu_seqlens_k"])
+            return time.perf_counter() - t0
+
+        n = min(S, max(threads, 16))
+        t = run(n)
+        for _ in range(2):   # the fixed cost of gathering the keys fades as n grows
+            n = int(min(S, max(n, n * budget_s / max(t, 1e-3))))
+            t = run(n)
+        res[name] = {"mode": "sample", "rows": n, "heads": 1, "of_row_heads": S * H,
+                     "seconds": round(t, 3), "tflops": flops * n / (S * H) / t / 1e12,
+                     "extrapolated_full_seconds": round(t * (S * H) / n, 1)}
+    inp = gen.workload_inputs(DECODE)
+    t0 = time.perf_counter()
+    oracle.paged_decode(inp["query"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["seq_lens"])
+    t = time.perf_counter() - t0
+    res[DECODE] = {"mode": "full", "seconds": round(t, 4), "gbs": decode_bytes(inp) / t / 1e9}
+    for v in res.values():
+        for key in ("tflops", "gbs"):
+            if key in v:
+                v[key] = float(f"{v[key]:.4g}")
+    return {"cores": threads, "kind": "oracle", "per_config": res}
 
 
 def copy_reference(torch, dev, args):
@@ -326,6 +447,9 @@ def main():
     ap.add_argument("--shapes", choices=["prefill", "decode", "chunk"], default=None,
                     help="time every row of that operator page's Shapes table (one JSON line "
                          "per row) and exit")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads after the step (counter runs use this "
+                         "so that each kernel name in their output is one workload)")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
                          "(no GPU needed)")
@@ -400,19 +524,21 @@ def main():
            torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        a, b, c, d = ev[i]
-        a.record()
-        if do_prefill:
-            prefill_call()
-        b.record()
-        c.record()
-        if do_decode:
-            decode_call(args.warmup + i)
-        d.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    clock = ClockSampler()
+    with clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            a, b, c, d = ev[i]
+            a.record()
+            if do_prefill:
+                prefill_call()
+            b.record()
+            c.record()
+            if do_decode:
+                decode_call(args.warmup + i)
+            d.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     pre_ms = sorted(a.elapsed_time(b) for a, b, _, _ in ev)
     dec_ms = sorted(c.elapsed_time(d) for _, _, c, d in ev)
@@ -450,11 +576,66 @@ def main():
     tflops = flops / (pre_avg * 1e-3) / 1e12 if do_prefill else 0.0
     gbs = dbytes / (dec_avg * 1e-3) / 1e9 if do_decode else 0.0
 
+    # The other benchmark workloads (page rows 11, 4 and 8 of the prefill
+    # Shapes table), each timed on its own: back-to-back launches bracketed by
+    # one event pair; the 276-token one, a few microseconds of work, also as
+    # 20 calls captured in a HIP graph and replayed (no per-call host path).
+    configs = {}
+    if args.only is None and p_name == PREFILL and not args.no_configs:
+        from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
+        for name in PREFILL_CONFIGS:
+            if name == PREFILL:
+                continue
+            x_host = gen.workload_inputs(name)
+            x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x_host.items()}
+            S, H, D = x_host["q"].shape
+            x_out = torch.empty_like(x["q"])
+            x_ws = torch.empty(attn_varlen_fwd_workspace_size(1, S, H, D), dtype=torch.uint8, device=dev)
+
+            def call(x=x, x_out=x_out, x_ws=x_ws):
+                attn_varlen_fwd(x["q"], x["k"], x["v"], x["cu_seqlens_q"], x["cu_seqlens_k"],
+                                max_seqlen_q=x["max_seqlen_q"], out=x_out, workspace=x_ws)
+
+            xf = prefill_flops(x_host)
+            reps = max(5, min(200, int(2e12 / xf)))
+            for _ in range(3):
+                call()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            rate = xf / (ms * 1e-3) / 1e12
+            entry = {"head_dim": D, "kernel": prefill_kernel(D)[1], "flops_per_launch": xf,
+                     "launches": reps, "avg_launch_us": round(ms * 1e3, 2), "achieved": round(rate, 1),
+                     "unit": "TFLOP/s", "frac": round(rate / PEAK_BF16_TFLOPS, 4)}
+            if ms < 0.2:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(20):
+                        call()
+                g.replay()
+                torch.cuda.synchronize()
+                a.record()
+                for _ in range(20):
+                    g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                gms = a.elapsed_time(b) / 400
+                entry["graph_us_per_launch"] = round(gms * 1e3, 2)
+                entry["graph_frac"] = round(xf / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            configs[name] = entry
+            del x, x_out, x_ws
+
     def traffic(prefix):
         return profiled_traffic(prefix, kernel_source_hash(KERNEL_SOURCES[prefix]))
 
     src_hash = kernel_source_hash(ALL_SOURCES)
-    pre_traffic = traffic("prefill_fwd_kernel") if p_name == PREFILL else None
+    pre_prefix, pre_label = prefill_kernel(int(p_host["q"].shape[2]))
+    pre_traffic = traffic(pre_prefix) if p_name == PREFILL else None
     dec_traffic = traffic("decode_partition_kernel")
     chunk_traffic = traffic("chunk_delta_out_kernel")
     cgbs = cbytes / (chunk_avg * 1e-3) / 1e9 if do_chunk else 0.0
@@ -486,10 +667,11 @@ def main():
             "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": pre_traffic,
-            "kernel": f"prefill_fwd_kernel<{int(p_host['q'].shape[2])}, bf16>",
+            "kernel": pre_label,
             "flops_per_launch": flops, "avg_launch_ms": round(pre_avg, 4),
             "min_launch_ms": round(pre_ms[0], 4),
             "median_launch_ms": round(pre_ms[len(pre_ms) // 2], 4),
+            "shader_clock": clock.summary(),
         },
         "decode": {
             "value": round(gbs, 1), "unit": "GB/s",
@@ -511,11 +693,15 @@ def main():
                 "avg_launch_us": round(chunk_avg * 1e3, 3),
             },
         },
+        "configs": configs,
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
         "kernel_source_hash": src_hash,
         "page_context": page_context(p_host),
     }
+    for name, entry in configs.items():
+        row = WORKLOAD_PAGE_ROWS.get(name)
+        entry["page_row"] = row
     # this run's per-launch times beside the pages' (context only)
     for key, us, on in (("prefill", pre_avg * 1e3, do_prefill), ("decode", dec_avg * 1e3, do_decode),
                         ("chunk", chunk_avg * 1e3, do_chunk)):
@@ -526,7 +712,10 @@ def main():
     if args.cpu_budget > 0 and args.only is None:
         result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
         if p_name == PREFILL and tflops > 0:
-            result["cpu_baseline"]["gpu_over_cpu"] = round(tflops / result["cpu_baseline"]["value"], 1)
+            cb = result["cpu_baseline"]
+            cb["gpu_over_cpu"] = round(tflops / cb["value"], 1)
+            cb["extrapolated_full_seconds"] = round(flops / (cb["value"] * 1e12), 1)
+            cb["workloads"] = oracle_per_config(max(1.0, args.cpu_budget / 5))["per_config"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
