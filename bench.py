@@ -162,75 +162,83 @@ def chunk_bytes(inp):
         + inp["v"].numel() * inp["v"].element_size()
 
 
-def cpu_baseline(budget_s):
-    """The oracle, as it stands, on a bounded sample of the prefill workload:
-    whole query rows (all keys) of the 16742-token sequence."""
-    import numpy as np
-    import oracle
-    from softmax_attention_flashattention_amd import inputs as gen
-    inp = gen.workload_inputs(PREFILL)
-    S, H, D = inp["q"].shape
-    rng = np.random.default_rng(0)
-    threads = oracle.num_threads()
-
-    def run(n):
-        rows = rng.integers(0, S, n)
-        heads = rng.integers(0, H, n)
-        t0 = time.perf_counter()
-        oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"],
-                               inp["cu_seqlens_k"], rows, heads)
-        return time.perf_counter() - t0
-
-    n = max(threads, 8)
-    t = run(n)
-    n = int(max(n, min(200000, n * (budget_s / max(t, 1e-3)))))
-    t = run(n)
-    flops = 4.0 * n * S * D          # each row: S keys, QK^T and PV
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} (query row, head) pairs of {PREFILL}, each against all {S} keys, "
-                      f"float64, {t:.1f} s"}
-
-
-def oracle_per_config(budget_s):
-    """The oracle, as it stands, on each benchmark workload: in full where that
-    takes seconds (the 276-token prefill, the decode workload), else on the
-    first n query rows of head 0 (one query segment of n rows against all of
-    the sequence's keys: the definition for those rows, through the same
-    whole-workload entry point), with the full-workload time extrapolated as
-    seconds x (rows x heads) / n and labelled as such.  n is sized to about
-    budget_s seconds of CPU work."""
+def oracle_prefill_sample(name, budget_s):
+    """The oracle's whole-workload prefill entry point on the first n query
+    rows of head 0 of a prefill workload (one query segment of n rows against
+    all of the sequence's keys: the definition for those rows, computed the
+    way a whole run computes them), n sized to about budget_s seconds."""
     import oracle
     import torch
+    from softmax_attention_flashattention_amd import inputs as gen
+    inp = gen.workload_inputs(name)
+    S, H, D = inp["q"].shape
+    k, v = inp["k"][:, :1].contiguous(), inp["v"][:, :1].contiguous()
+
+    def run(n):
+        q = inp["q"][:n, :1].contiguous()
+        cu_q = torch.tensor([0, n], dtype=torch.int32)
+        t0 = time.perf_counter()
+        oracle.varlen_fwd(q, k, v, cu_q, inp["cu_seqlens_k"])
+        return time.perf_counter() - t0
+
+    n = min(S, max(oracle.num_threads(), 16))
+    t = run(n)
+    runs = [(n, t)]
+    for _ in range(2):
+        n = int(min(S, max(n, n * budget_s / max(t, 1e-3))))
+        t = run(n)
+        runs.append((n, t))
+    # A whole run gathers each head's keys and values once, then computes
+    # its rows: per head, time = a + b x rows.  a and b from the smallest and
+    # largest sample; the whole workload takes H (a + b S).
+    (n1, t1), (n2, t2) = runs[0], runs[-1]
+    b = (t2 - t1) / (n2 - n1) if n2 > n1 else t2 / n2
+    a = max(0.0, t2 - b * n2)
+    b = (t2 - a) / n2
+    flops = prefill_flops(inp)
+    return {"mode": "sample", "rows": n, "heads": 1, "of_row_heads": S * H, "keys": S,
+            "seconds": round(t, 3), "tflops": flops * n / (S * H) / t / 1e12,
+            "extrapolated_full_seconds": round(H * (a + b * S), 1),
+            "extrapolation": f"per head {a:.3g} s for the keys + {b:.3g} s per row, times {H} heads"}
+
+
+def cpu_baseline(budget_s):
+    """The oracle, as it stands, on a bounded sample of the step's prefill
+    workload: its first query rows of head 0, each against all keys."""
+    import oracle
+    smp = oracle_prefill_sample(PREFILL, budget_s)
+    return {"value": smp["tflops"], "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the first {smp['rows']} query rows of head 0 of {PREFILL} (of "
+                      f"{smp['of_row_heads']} (row, head) pairs), each against all {smp['keys']} keys, "
+                      f"through the oracle's whole-workload prefill entry point, float64, "
+                      f"{smp['seconds']:.1f} s",
+            "extrapolated_full_seconds": smp["extrapolated_full_seconds"],
+            "_sample": smp}
+
+
+def oracle_per_config(budget_s, known=None):
+    """The oracle, as it stands, on each benchmark workload: in full where that
+    takes seconds (the 276-token prefill, the decode workload), else on a
+    sample (oracle_prefill_sample) with the full-workload time extrapolated as
+    seconds x (rows x heads) / n and labelled as such.  `known` holds samples
+    already taken (by workload name)."""
+    import oracle
     from softmax_attention_flashattention_amd import inputs as gen
     threads = oracle.num_threads()
     res = {}
     for name in PREFILL_CONFIGS:
+        if known and name in known:
+            res[name] = dict(known[name])
+            continue
         inp = gen.workload_inputs(name)
         S, H, D = inp["q"].shape
-        flops = prefill_flops(inp)
         if S * S * H <= 1 << 24:
             t0 = time.perf_counter()
             oracle.varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"])
             t = time.perf_counter() - t0
-            res[name] = {"mode": "full", "seconds": round(t, 4), "tflops": flops / t / 1e12}
+            res[name] = {"mode": "full", "seconds": round(t, 4), "tflops": prefill_flops(inp) / t / 1e12}
             continue
-        k, v = inp["k"][:, :1].contiguous(), inp["v"][:, :1].contiguous()
-
-        def run(n):
-            q = inp["q"][:n, :1].contiguous()
-            cu_q = torch.tensor([0, n], dtype=torch.int32)
-            t0 = time.perf_counter()
-            oracle.varlen_fwd(q, k, v, cu_q, inp["cu_seqlens_k"])
-            return time.perf_counter() - t0
-
-        n = min(S, max(threads, 16))
-        t = run(n)
-        for _ in range(2):   # the fixed cost of gathering the keys fades as n grows
-            n = int(min(S, max(n, n * budget_s / max(t, 1e-3))))
-            t = run(n)
-        res[name] = {"mode": "sample", "rows": n, "heads": 1, "of_row_heads": S * H,
-                     "seconds": round(t, 3), "tflops": flops * n / (S * H) / t / 1e12,
-                     "extrapolated_full_seconds": round(t * (S * H) / n, 1)}
+        res[name] = oracle_prefill_sample(name, budget_s)
     inp = gen.workload_inputs(DECODE)
     t0 = time.perf_counter()
     oracle.paged_decode(inp["query"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["seq_lens"])
@@ -597,7 +605,7 @@ def main():
                                 max_seqlen_q=x["max_seqlen_q"], out=x_out, workspace=x_ws)
 
             xf = prefill_flops(x_host)
-            reps = max(5, min(200, int(2e12 / xf)))
+            reps = max(10, min(2000, int(5e13 / xf)))   # 25 ms or more of launches
             for _ in range(3):
                 call()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -710,12 +718,13 @@ def main():
     if args.only is not None:
         result["only"] = args.only
     if args.cpu_budget > 0 and args.only is None:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+        cb = cpu_baseline(args.cpu_budget)
+        smp = cb.pop("_sample")
         if p_name == PREFILL and tflops > 0:
-            cb = result["cpu_baseline"]
             cb["gpu_over_cpu"] = round(tflops / cb["value"], 1)
-            cb["extrapolated_full_seconds"] = round(flops / (cb["value"] * 1e12), 1)
-            cb["workloads"] = oracle_per_config(max(1.0, args.cpu_budget / 5))["per_config"]
+        cb["workloads"] = oracle_per_config(max(1.0, args.cpu_budget / 5),
+                                            known={PREFILL: smp})["per_config"]
+        result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -1,4 +1,6 @@
-// prefill_kernel.hpp -- non-causal varlen prefill attention for gfx950.
+// prefill_kernel.hpp -- non-causal varlen prefill attention for gfx950,
+// head_dim 72 (head_dim 128 runs prefill_d128_kernel.hpp); also the
+// parameter block and the key-range merge kernel both prefill kernels share.
 //
 // Computes, per sequence and head, out = softmax(scale * Q K^T) V (the
 // operator of the atrex-bench page "attention_forward" #001, Reference
@@ -7,16 +9,14 @@
 //
 // Work decomposition.  One workgroup of WAVES waves owns a tile of BM = 32
 // WAVES query rows of one (sequence, head); each wave owns 32 of those rows.
-// WAVES is 4 (BM 128), or 8 (BM 256) for head_dim 72 when the work items fill
-// the device at least once: twice the rows then share each K/V tile in LDS,
-// halving the tile DMA per flop, the costliest part at that head_dim.  The
-// workgroup streams the sequence's keys and values in tiles of BN = 64 rows
-// through double-buffered LDS.  The tiles go from global memory straight
-// into LDS (buffer loads with the LDS destination bit).  head_dim 128 lays
-// them out unpadded with an XOR swizzle of the 16-byte chunks of each row so
-// that the MFMA operand reads hit distinct banks; head_dim 72 uses padded
-// rows whose pitch spreads the reads over the banks, with the DMA lanes that
-// would land on pad chunks masked off.
+// WAVES is 4 (BM 128), or 8 (BM 256) when the work items fill the device at
+// least once: twice the rows then share each K/V tile in LDS, halving the
+// tile DMA per flop, the costliest part at this head_dim.  The workgroup
+// streams the sequence's keys and values in tiles of BN = 64 rows through
+// double-buffered LDS.  The tiles go from global memory straight into LDS
+// (buffer loads with the LDS destination bit) as padded rows whose pitch
+// spreads the operand reads over the banks, with the DMA lanes that would
+// land on pad chunks masked off.
 //
 // Both contractions run on 32x32x16 MFMA with fp32 accumulation, computed
 // transposed so that each lane owns one query row:
@@ -38,10 +38,10 @@
 // the end of the sequence get weight 0 by selection, which holds for c = 0
 // as well (where c * -inf would be NaN).
 //
-// head_dim 72 pads the QK^T contraction to 80 (five k-steps of 16; the K pad
-// columns are zero) and the V^T row blocks to 96; column 72 of the V tile
-// holds 1.0, so row 72 of O^T accumulates the row sum of the 16-bit P that
-// actually multiplied V (the padding does useful work instead of a VALU sum).
+// The QK^T contraction is padded to 80 (five k-steps of 16; the K pad columns
+// are zero) and the V^T row blocks to 96; column 72 of the V tile holds 1.0,
+// so row 72 of O^T accumulates the row sum of the 16-bit P that actually
+// multiplied V (the padding does useful work instead of a VALU sum).
 #pragma once
 
 #include <type_traits>
@@ -67,27 +67,16 @@ struct PrefillParams {
 };
 
 template <int D> struct PrefillShape;
-template <> struct PrefillShape<128> {
-    static constexpr int KSTEPS = 8;    // QK^T contraction steps of 16
-    static constexpr int DBLK = 4;      // O^T row blocks of 32
-    static constexpr bool SWIZZLE = true;  // whole rows per DMA instruction, chunks XOR-swizzled
-    static constexpr int KPITCH = 128;  // unpadded rows; chunks XOR-swizzled
-    static constexpr int VPITCH = 128;
-    static constexpr int ONES_COL = -1;
-};
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
     static constexpr int DBLK = 3;      // 72 padded to 96
-    static constexpr bool SWIZZLE = false;  // padded rows; DMA slots on pad chunks masked off
     static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
 };
 
 constexpr int kPrefillBN = 64;
-// Workgroup size: WAVES waves of 32 query rows each (BM = 32 WAVES rows).
-// head_dim 128 runs 4 waves (8 measured level: the two waves of a SIMD then
-// belong to one workgroup and move in lockstep); head_dim 72 runs 4 or 8.
+// Workgroup size: WAVES (4 or 8) waves of 32 query rows each (BM = 32 WAVES rows).
 constexpr int prefill_bm(int waves) { return 32 * waves; }
 constexpr int prefill_threads(int waves) { return 64 * waves; }
 
@@ -166,9 +155,10 @@ void prefill_fwd_kernel(PrefillParams p)
     const uint16_t *v_head = p.v + ka * rs + head * D;
     const float c = p.scale_log2e;
 
-    if constexpr (S::ONES_COL >= 0) {
+    {
         // constant pad columns of both buffers: K cols 72..79 = 0,
         // V col 72 = 1, V cols 73..95 = 0
+        static_assert(S::ONES_COL == 72 && KP >= 80 && VP >= 96, "pad columns");
         const uint4 z = {0u, 0u, 0u, 0u};
         const uint4 one = {T::one_bits, 0u, 0u, 0u};
         for (int r = tid; r < BN; r += kPrefillThreads) {
@@ -214,42 +204,24 @@ void prefill_fwd_kernel(PrefillParams p)
     };
 
     // Direct path.  A DMA instruction fills 1 KiB of LDS (lane i -> bytes
-    // 16 i .. 16 i + 15), each lane from its own global address.
-    // head_dim 128: a tile is 16 instructions of 4 rows; instruction j of
-    // wave w fills LDS rows RW w + 4 j .. +3, RW = 64 / WAVES.  Row R keeps
-    // logical chunk c at position c ^ (R % 16) for K and c ^ 4 (R % 4) for V.
-    // head_dim 72: the padded tile (KP or VP elements a row) is BN KP / 512
-    // instructions; instruction n = WAVES j + w covers the 16-byte slots
-    // 64 n .. 64 n + 63 of the tile, slot s being chunk s % (pitch / 8) of
-    // row s / (pitch / 8); lanes on the pad chunks (>= 9) are masked off,
-    // so the constant pad columns set up below stay as they are.
-    constexpr bool SWZ = S::SWIZZLE;
+    // 16 i .. 16 i + 15), each lane from its own global address.  The padded
+    // tile (KP or VP elements a row) is BN KP / 512 instructions; instruction
+    // n = WAVES j + w covers the 16-byte slots 64 n .. 64 n + 63 of the tile,
+    // slot s being chunk s % (pitch / 8) of row s / (pitch / 8); lanes on the
+    // pad chunks (>= 9) are masked off, so the constant pad columns set up
+    // above stay as they are.
     constexpr int NKI = BN * KP / 512, NVI = BN * VP / 512;   // DMA instructions per tile
     constexpr int DJK = (NKI + WAVES - 1) / WAVES;            // ... per wave (at most)
     constexpr int DJV = (NVI + WAVES - 1) / WAVES;
-    constexpr int RW = 64 / WAVES;      // tile rows per wave (head_dim 128)
-    // (fixed size: a local array sized by a template-dependent constant here
-    // makes hipcc drop the kernel's host launch stub for head_dim 128)
     // The whole byte offset of every lane goes in the VGPR offset: the
     // buffer range check covers that offset only (not the scalar one), so
     // this is what turns rows past the sequence's last key into zeros.
     uint32_t dk_off[4] = {0u, 0u, 0u, 0u};
     uint32_t dv_off[4] = {0u, 0u, 0u, 0u};
     bool dk_act[4] = {false, false, false, false}, dv_act[4] = {false, false, false, false};
-    if constexpr (SWZ) {
-        const int rsub = lane >> 4, pos = lane & 15;
-#pragma unroll
-        for (int j = 0; j < DJK; ++j) {
-            const int R = RW * wave + 4 * j + rsub;
-            dk_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (R & 15));
-        }
-#pragma unroll
-        for (int j = 0; j < DJV; ++j) {
-            const int R = RW * wave + 4 * j + rsub;
-            dv_off[j] = static_cast<uint32_t>(R) * row_bytes + 16u * static_cast<uint32_t>(pos ^ (4 * (R & 3)));
-        }
-    } else {
+    {
         constexpr int KC = KP / 8, VC = VP / 8;   // 16-byte slots per padded row
+        static_assert(DJK <= 4 && DJV <= 4, "offset arrays");
 #pragma unroll
         for (int j = 0; j < DJK; ++j) {
             const int s = 64 * (WAVES * j + wave) + lane;
@@ -266,26 +238,14 @@ void prefill_fwd_kernel(PrefillParams p)
 
     // one DMA instruction (number j of this wave) of a K or V tile
     auto dma_k = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
-        if constexpr (SWZ) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void *)(kbuf(par) + (RW * wave_s + 4 * j) * KP), 16, dk_off[j], 0, 0, 0);
-        } else {
-            const int n = WAVES * j + wave_s;
-            if (n < NKI && dk_act[j])
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(kbuf(par) + 512 * n), 16, dk_off[j],
-                                                         0, 0, 0);
-        }
+        const int n = WAVES * j + wave_s;
+        if (n < NKI && dk_act[j])
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(kbuf(par) + 512 * n), 16, dk_off[j], 0, 0, 0);
     };
     auto dma_v = [&](const __amdgpu_buffer_rsrc_t &r, auto par, int j) {
-        if constexpr (SWZ) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void *)(vbuf(par) + (RW * wave_s + 4 * j) * VP), 16, dv_off[j], 0, 0, 0);
-        } else {
-            const int n = WAVES * j + wave_s;
-            if (n < NVI && dv_act[j])
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dv_off[j],
-                                                         0, 0, 0);
-        }
+        const int n = WAVES * j + wave_s;
+        if (n < NVI && dv_act[j])
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(vbuf(par) + 512 * n), 16, dv_off[j], 0, 0, 0);
     };
     auto load_k = [&](int t, auto par) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(k_head + static_cast<int64_t>(t) * BN * rs, tile_bytes(t));
@@ -307,17 +267,14 @@ void prefill_fwd_kernel(PrefillParams p)
     // K rows for S^T: row 32 kb2 + l32, chunk 2 ks + hi
     int k_rd[S::KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks)
-        k_rd[ks] = SWZ ? l32 * KP + 8 * ((2 * ks + hi) ^ (l32 & 15)) : l32 * KP + 16 * ks + 8 * hi;
+    for (int ks = 0; ks < S::KSTEPS; ++ks) k_rd[ks] = l32 * KP + 16 * ks + 8 * hi;
     // V^T by transposed reads: row 16 kc + tr_row (+8), column 32 db + tr_col
     const int g16 = lane >> 4;
     const int tr_row = 4 * (g16 >> 1) + ((lane & 15) >> 2);
     const int tr_col = 16 * (g16 & 1) + 4 * (lane & 3);
     int v_rd[S::DBLK];
 #pragma unroll
-    for (int db = 0; db < S::DBLK; ++db)
-        v_rd[db] = SWZ ? tr_row * VP + 8 * ((4 * db + (tr_col >> 3)) ^ (4 * (tr_row & 3))) + (tr_col & 7)
-                          : tr_row * VP + 32 * db + tr_col;
+    for (int db = 0; db < S::DBLK; ++db) v_rd[db] = tr_row * VP + 32 * db + tr_col;
 
     // S^T = K Q^T for the two 32-key blocks of a tile
     auto compute_s = [&](auto par, f32x16 (&sacc)[2]) {
@@ -347,7 +304,6 @@ void prefill_fwd_kernel(PrefillParams p)
 
     float m_run = -INFINITY;   // running max of c*s for this lane's query (log2 domain)
     float m_lim = -INFINITY;   // raw scores above this may need the running max raised
-    float l_run0 = 0.f, l_run1 = 0.f;   // this lane's partial row sums (two chains)
     f32x16 oacc[S::DBLK];
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db)
@@ -405,8 +361,6 @@ void prefill_fwd_kernel(PrefillParams p)
             // score the exact test would take fails the cheap one
             const float lim = (m_run + kRescaleThreshold) / c;
             m_lim = lim - fabsf(lim) * 0x1p-16f;
-            l_run0 *= alpha;
-            l_run1 *= alpha;
 #pragma unroll
             for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
@@ -473,8 +427,8 @@ void prefill_fwd_kernel(PrefillParams p)
         // The NS MFMAs of S(t+1) = K(t+1) Q^T, in the order ks outer, kb2
         // inner (two independent accumulator chains), each K operand read KD
         // MFMAs ahead.  Between consecutive MFMAs sits a slice of the softmax
-        // of tile t: exponentials, 16-bit packing and row sums of its 16 value
-        // pairs.
+        // of tile t: exponentials and 16-bit packing of its 16 value pairs
+        // (the row sums come from the ones column of V).
         const uint16_t *kt = kbuf(npar);
         auto kop = [&](int i) { return kop_at(kt, i); };
         s16x8 kq[KD + 1];
@@ -482,7 +436,7 @@ void prefill_fwd_kernel(PrefillParams p)
         for (int i = 0; i < KD; ++i) kq[i] = kq_pre[i];   // read during the previous step
         const f32x16 zero = {};
         uint32_t pw[16];
-        // exponentials, 16-bit packing and row sums of value pairs [pb, pe)
+        // exponentials and 16-bit packing of value pairs [pb, pe)
         // of tile t (pair pi = keys 2 (pi & 7), +1 of 32-key block pi >> 3)
         auto exp_pairs = [&](int pb, int pe) {
 #pragma unroll
@@ -500,17 +454,6 @@ void prefill_fwd_kernel(PrefillParams p)
                     }
                 }
                 pw[pi] = pack2<T>(p0, p1);
-                if constexpr (S::ONES_COL < 0) {
-                    // the empty asm keeps each sum in its slice (otherwise the
-                    // compiler sinks the whole chain to the end of the loop)
-                    if (pi & 1) {
-                        l_run1 = T::sum2(pw[pi], l_run1);
-                        asm volatile("" : "+v"(l_run1));
-                    } else {
-                        l_run0 = T::sum2(pw[pi], l_run0);
-                        asm volatile("" : "+v"(l_run0));
-                    }
-                }
             }
         };
         // The VALU work of a tile is spread over all its MFMAs: pairs
@@ -572,16 +515,10 @@ void prefill_fwd_kernel(PrefillParams p)
     if (t + 2 < t1) step(t + 2, P0{}, P1{}, sa, sb, Masked{});
 
     // ---- epilogue: normalise, round to 16 bits, store rows inside the segment
-    float l_tot;
-    if constexpr (S::ONES_COL < 0) {
-        const float l_run = l_run0 + l_run1;
-        l_tot = l_run + swap_halves(l_run);
-    } else {
-        // row 72 of O^T = block 2, register 4, lanes 0..31
-        const float lv = oacc[2][4];
-        const float other = swap_halves(lv);
-        l_tot = hi ? other : lv;
-    }
+    // the row sum: row 72 of O^T = block 2, register 4, lanes 0..31
+    const float lv = oacc[2][4];
+    const float other = swap_halves(lv);
+    const float l_tot = hi ? other : lv;
     if (nparts > 1) {
         // a key range of a split item: unnormalised O^T, running max and row
         // sum to the workspace; prefill_merge_kernel combines the ranges
