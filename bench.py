@@ -412,6 +412,71 @@ def shapes_rows(torch, dev, which):
         del x, d, out
 
 
+def decode_partition_sweep(torch, dev):
+    """Every row of the decode Shapes table, plus three shapes with few long
+    contexts, timed with the library's own partition choice (partition_size
+    0) and with forced 16- to 512-token partitions: per-launch time of 20
+    calls captured in a HIP graph and replayed 30 times.  One JSON line per
+    shape; `max_abs_diff` compares every forced split with the automatic
+    one."""
+    sys.path.insert(0, os.path.join(ROOT, "tests", "golden"))
+    import shapes
+    from softmax_attention_flashattention_amd import attn_paged_decode, attn_paged_decode_num_partitions
+    from softmax_attention_flashattention_amd import inputs as gen
+
+    def graph_us(call, per_graph=20, reps=30):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * per_graph) * 1e3
+
+    long_ctx = [dict(row="long-1", num_seqs=1, ctx_len=1024, num_query_heads=16, num_kv_heads=2,
+                     head_size=128, dtype="bf16"),
+                dict(row="long-2", num_seqs=4, ctx_len=2048, num_query_heads=32, num_kv_heads=8,
+                     head_size=128, dtype="bf16"),
+                dict(row="long-3", num_seqs=1, ctx_len=4096, num_query_heads=8, num_kv_heads=1,
+                     head_size=128, dtype="bf16")]
+    for r in list(shapes.decode_rows()) + long_ctx:
+        x = gen.decode_inputs(r["num_seqs"], r["ctx_len"], r["num_query_heads"], r["num_kv_heads"],
+                              r["head_size"], seed=3000, dtype=r["dtype"])
+        d = {k: v.to(dev) for k, v in x.items()}
+        maxb = x["block_tables"].shape[1]
+        times, diff, auto = {}, 0.0, None
+        for ps in (0, 16, 32, 64, 128, 256, 512):
+            if ps >= 2 * max(r["ctx_len"], 16):
+                continue
+            out = torch.empty_like(d["query"])
+            call = lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"],
+                                             d["block_tables"], d["seq_lens"], out=out,
+                                             partition_size=ps)
+            times["auto" if ps == 0 else str(ps)] = round(graph_us(call), 2)
+            call()
+            torch.cuda.synchronize()
+            if auto is None:
+                auto = out.float().clone()
+            diff = max(diff, (out.float() - auto).abs().max().item())
+        print(json.dumps({"decode_partitions": r["row"], "num_seqs": r["num_seqs"],
+                          "ctx_len": r["ctx_len"], "num_query_heads": r["num_query_heads"],
+                          "num_kv_heads": r["num_kv_heads"], "head_size": r["head_size"],
+                          "dtype": r["dtype"],
+                          "auto_partitions": attn_paged_decode_num_partitions(
+                              r["num_seqs"], r["num_kv_heads"], maxb, 16),
+                          "graph_us_by_partition_tokens": times, "max_abs_diff": diff}), flush=True)
+        del x, d
+
+
 def page_context(p_host):
     """The pages' own times for the timed workloads (Shapes tables stored under
     tests/golden): T_SOL on hardware the pages label only "XPU-A", T_Prod on
@@ -458,6 +523,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other prefill workloads after the step (counter runs use this "
                          "so that each kernel name in their output is one workload)")
+    ap.add_argument("--decode-partitions", action="store_true",
+                    help="time the decode Shapes rows and three few-long-context shapes with the "
+                         "automatic and with forced context partitions (one JSON line each) and exit")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
                          "(no GPU needed)")
@@ -481,6 +549,8 @@ def main():
         return copy_reference(torch, dev, args)
     if args.shapes:
         return shapes_rows(torch, dev, args.shapes)
+    if args.decode_partitions:
+        return decode_partition_sweep(torch, dev)
 
     p_name = args.prefill_workload
     p_host = gen.workload_inputs(p_name)

@@ -134,11 +134,14 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q,
  *  block_size     16 (others return ATTN_ERR_UNSUPPORTED)
  *  num_query_heads % num_kv_heads must be 0; the group size
  *                 num_query_heads / num_kv_heads must be at most 16
- *  partition_size tokens per split of the context (split-K); 0 picks the
- *                 library default.  A positive value must be a multiple of
- *                 block_size.  With more than one partition the kernel writes
- *                 per-partition (max, sum, partial output) into `workspace`
- *                 and a second kernel merges them by log-sum-exp.
+ *  partition_size tokens per split of the context (split-K); a positive
+ *                 value must be a multiple of block_size.  0 lets the
+ *                 library choose: 512 tokens, halved down to 128 while
+ *                 num_seqs x num_kv_heads x partitions (one workgroup each)
+ *                 is below the current device's compute-unit count.  With
+ *                 more than one partition the kernel writes per-partition
+ *                 (max, sum, partial output) into `workspace` and a second
+ *                 kernel merges them by log-sum-exp.
  *  workspace      device memory of attn_paged_decode_workspace_size(...)
  *                 bytes, 256-byte aligned; may be NULL when that size is 0
  *  out            [num_seqs, num_query_heads, head_size], dtype; every row is
@@ -186,21 +189,23 @@ int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void
                               int32_t partition_size, void *out, void *stream);
 
 /*
- * Number of context partitions attn_paged_decode will use for these sizes
- * (1 means no split and no workspace).  Returns a negative attn_status
- * value on invalid sizes.
+ * Number of context partitions attn_paged_decode will use for these sizes on
+ * the current device (1 means no split and no workspace).  Returns a
+ * negative attn_status value on invalid sizes.
  */
-int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,
+int32_t attn_paged_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
+                                         int32_t max_blocks_per_seq, int32_t block_size,
                                          int32_t partition_size);
 
 /*
- * Workspace bytes attn_paged_decode needs for these sizes (0 when one
- * partition suffices).  Returns 0 on invalid sizes as well; the decode call
- * itself reports those.
+ * Workspace bytes attn_paged_decode needs for these sizes on the current
+ * device (0 when one partition suffices).  Returns 0 on invalid sizes as
+ * well; the decode call itself reports those.
  */
 size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads,
-                                        int32_t head_size, int32_t max_blocks_per_seq,
-                                        int32_t block_size, int32_t partition_size);
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t max_blocks_per_seq, int32_t block_size,
+                                        int32_t partition_size);
 
 /*
  * attn_chunk_delta_out -- output step of chunked gated delta-rule linear

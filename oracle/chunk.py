@@ -46,6 +46,10 @@ def load(path=None):
     if path is not None:
         return _declare(ctypes.CDLL(path))
     if _lib is None:
+        override = os.environ.get("ATTN_CHUNK_ORACLE_LIB")   # another build of the same source
+        if override:
+            _lib = _declare(ctypes.CDLL(override))
+            return _lib
         if not os.path.exists(_LIB_PATH):
             build()
         _lib = _declare(ctypes.CDLL(_LIB_PATH))

@@ -58,9 +58,9 @@ def _load():
     lib.attn_paged_decode_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i64, f32,
                                               i32, i32, P, P]
     lib.attn_paged_decode_noalloc.restype = ctypes.c_int
-    lib.attn_paged_decode_num_partitions.argtypes = [i32, i32, i32]
+    lib.attn_paged_decode_num_partitions.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_paged_decode_num_partitions.restype = i32
-    lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.attn_paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.attn_paged_decode_workspace_size.restype = sz
     lib.attn_chunk_delta_out.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                          P, P]
@@ -154,21 +154,26 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
     return out
 
 
-def attn_paged_decode_num_partitions(max_blocks_per_seq, block_size, partition_size=0):
-    """Context partitions the decode call will use (calls the C function)."""
-    n = _load().attn_paged_decode_num_partitions(int(max_blocks_per_seq), int(block_size),
+def attn_paged_decode_num_partitions(num_seqs, num_kv_heads, max_blocks_per_seq, block_size,
+                                     partition_size=0):
+    """Context partitions the decode call will use on the current device
+    (calls the C function)."""
+    n = _load().attn_paged_decode_num_partitions(int(num_seqs), int(num_kv_heads),
+                                                 int(max_blocks_per_seq), int(block_size),
                                                  int(partition_size))
     if n < 0:
         raise AttnError("attn_paged_decode_num_partitions", -n)
     return n
 
 
-def attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, max_blocks_per_seq,
-                                     block_size, partition_size=0):
-    """Workspace bytes for a decode call (calls the C function)."""
+def attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads, head_size,
+                                     max_blocks_per_seq, block_size, partition_size=0):
+    """Workspace bytes for a decode call on the current device (calls the C
+    function)."""
     return _load().attn_paged_decode_workspace_size(int(num_seqs), int(num_query_heads),
-                                                    int(head_size), int(max_blocks_per_seq),
-                                                    int(block_size), int(partition_size))
+                                                    int(num_kv_heads), int(head_size),
+                                                    int(max_blocks_per_seq), int(block_size),
+                                                    int(partition_size))
 
 
 def _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out):
@@ -210,14 +215,14 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
     query [num_seqs, Hq, D]; k_cache [num_blocks, Hkv, D/8, block_size, 8];
     v_cache [num_blocks, Hkv, D, block_size]; block_tables int32
     [num_seqs, max_blocks_per_seq]; seq_lens int32 [num_seqs].  ``scale``
-    defaults to D**-0.5.  ``partition_size`` (tokens, 0 = library default)
-    sets the split-K granularity; the workspace it needs is allocated here
-    unless one is passed.
+    defaults to D**-0.5.  ``partition_size`` (tokens; 0 lets the library
+    choose) sets the split-K granularity; the workspace it needs is
+    allocated here unless one is passed.
     """
     sizes, scale, out = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out)
     num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
-    ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size, maxb,
-                                                block_size, partition_size)
+    ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads,
+                                                head_size, maxb, block_size, partition_size)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
     elif workspace is not None:

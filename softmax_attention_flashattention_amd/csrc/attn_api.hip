@@ -23,6 +23,7 @@ static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTE
 namespace {
 
 constexpr int kDefaultPartitionTokens = 512;
+constexpr int kMinAutoPartitionTokens = 128;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -202,11 +203,42 @@ int dispatch_decode(const attn::DecodeParams &p, int head_size, int64_t grid, hi
                             : dispatch_decode_g<T, 256>(p, grid, stream);
 }
 
-int partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size, int *part_blocks)
+// Compute units of the current device (256 when the runtime cannot tell).
+int device_cus()
 {
-    if (max_blocks_per_seq < 0 || block_size <= 0 || partition_size < 0) return -ATTN_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Tokens per context partition.  Left to the library (partition_size 0):
+// kDefaultPartitionTokens, halved down to kMinAutoPartitionTokens while the
+// workgroups (sequence x KV head x partition) would leave compute units
+// without one.  Few long contexts then spread over the device (graph
+// replayed: 1 sequence x 2 KV heads x 1024 tokens 29.4 -> 13.3 us, 4 x 8 x
+// 2048 23.1 -> 16.6 us, 1 x 1 x 4096 32.2 -> 20.2 us); shorter partitions
+// (one block per wave) were slower on most of the small rows measured,
+// their merge and per-workgroup start costing more than they spread.
+int partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq,
+                     int32_t block_size, int32_t partition_size)
+{
+    if (partition_size > 0) return partition_size;
+    const int64_t cus = device_cus();
+    const int64_t ctx = max_blocks_per_seq * block_size;
+    int pt = kDefaultPartitionTokens;
+    while (pt > kMinAutoPartitionTokens && num_seqs * num_kv_heads * ((ctx + pt - 1) / pt) < cus) pt /= 2;
+    return pt;
+}
+
+int partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
+               int32_t partition_size, int *part_blocks)
+{
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || block_size <= 0 || partition_size < 0)
+        return -ATTN_ERR_INVALID_ARG;
     if (partition_size % block_size) return -ATTN_ERR_INVALID_ARG;
-    const int pt = partition_size > 0 ? partition_size : kDefaultPartitionTokens;
+    const int pt = partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
     int pb = pt / block_size;
     if (pb < 1) pb = 1;
     if (part_blocks) *part_blocks = pb;
@@ -325,18 +357,18 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
                                     : launch_prefill<72, attn::Fp16, 4>(p, pl.grid, s);
 }
 
-int32_t attn_paged_decode_num_partitions(int32_t max_blocks_per_seq, int32_t block_size,
-                                         int32_t partition_size)
+int32_t attn_paged_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                         int32_t block_size, int32_t partition_size)
 {
-    return partitions(max_blocks_per_seq, block_size, partition_size, nullptr);
+    return partitions(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size, nullptr);
 }
 
-size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads, int32_t head_size,
-                                        int32_t max_blocks_per_seq, int32_t block_size,
+size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                                        int32_t head_size, int32_t max_blocks_per_seq, int32_t block_size,
                                         int32_t partition_size)
 {
     if (num_seqs < 0 || num_query_heads <= 0 || head_size <= 0) return 0;
-    const int np = partitions(max_blocks_per_seq, block_size, partition_size, nullptr);
+    const int np = partitions(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size, nullptr);
     if (np <= 1) return 0;
     const size_t rows = static_cast<size_t>(num_seqs) * num_query_heads * np;
     const size_t ml = (rows * 2 * sizeof(float) + 255) / 256 * 256;
@@ -385,7 +417,8 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
 {
     const int G = num_query_heads / num_kv_heads;
     int part_blocks = 1;
-    const int np = partitions(max_blocks_per_seq, block_size, partition_size, &part_blocks);
+    const int np = partitions(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size,
+                              &part_blocks);
     if (np < 1) return ATTN_ERR_INVALID_ARG;
     const int64_t grid = static_cast<int64_t>(num_seqs) * num_kv_heads * np;
     if (grid > INT32_MAX || static_cast<int64_t>(num_seqs) * num_query_heads > INT32_MAX)
@@ -401,8 +434,8 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     p.ws_ml = nullptr;
     p.ws_o = nullptr;
     if (np > 1) {
-        const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size,
-                                                             max_blocks_per_seq, block_size,
+        const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads,
+                                                             head_size, max_blocks_per_seq, block_size,
                                                              partition_size);
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return ATTN_ERR_WORKSPACE;
         const size_t rows = static_cast<size_t>(num_seqs) * num_query_heads * np;
@@ -456,7 +489,7 @@ int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void
                                      num_query_heads, num_kv_heads, head_size, block_size,
                                      max_blocks_per_seq, num_blocks, scale, dtype, partition_size, out);
     if (rc != ATTN_OK) return rc;
-    const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, head_size,
+    const size_t need = attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads, head_size,
                                                          max_blocks_per_seq, block_size, partition_size);
     if (need > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
     // set-up on the first call on a device (also when no split needs it)

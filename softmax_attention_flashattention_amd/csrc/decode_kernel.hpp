@@ -25,7 +25,8 @@
 //   V: dim 32 c + l / 2 of tokens 8 (l % 2) .. +7.
 // Both dot products run on v_dot2 (two 16-bit products summed into fp32):
 // q K^T with the 16-bit query, P V with the weights rounded to the 16-bit
-// type (like the P operand of the prefill kernel).  Scores need a 4-lane
+// type (like the P operand of the prefill kernel); the row sum adds up those
+// same rounded weights.  Scores need a 4-lane
 // reduction (v_permlane16/32_swap) and the block max and sum a 16-lane one
 // (DPP), all in VALU; the weights move from the token-owning lanes to the
 // dim-owning lanes through LDS.  At the end the four waves' (max, sum, partial output)
@@ -162,7 +163,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
                 const float m_new = fmaxf(m_run[g], bm);
                 const bool none = m_new == -INFINITY;
                 const float alpha = none ? 1.f : fast_exp2(m_run[g] - m_new);
-                const float pv = none ? 0.f : fast_exp2(sc - m_new);
+                // the weight as the 16-bit value that multiplies V, so that
+                // the row sum divides out exactly what the product summed
+                const float pv = T::to_f32(T::from_f32(none ? 0.f : fast_exp2(sc - m_new)));
                 const float ps = row16_sum(pv);
                 l_run[g] = l_run[g] * alpha + ps;
                 m_run[g] = m_new;

@@ -116,15 +116,25 @@ def test_decode_argument_errors(lib):
 
 
 def test_decode_workspace_rules(lib):
-    # 64 blocks per sequence at the default 512-token partition: 2 partitions
-    assert lib.attn_paged_decode_num_partitions(64, 16, 0) == 2
-    assert lib.attn_paged_decode_num_partitions(4, 16, 0) == 1
-    assert lib.attn_paged_decode_num_partitions(4, 16, 16) == 4
-    assert lib.attn_paged_decode_num_partitions(4, 16, 24) == -INVALID
-    need = lib.attn_paged_decode_workspace_size(4, 16, 128, 64, 16, 0)
-    rows = 4 * 16 * 2
-    assert need == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
-    assert lib.attn_paged_decode_workspace_size(4, 16, 128, 4, 16, 0) == 0
+    # (num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size)
+    # 64 x 16 workgroups fill the device at the default 512-token partition:
+    # 64 blocks per sequence give 2 partitions
+    assert lib.attn_paged_decode_num_partitions(64, 16, 64, 16, 0) == 2
+    assert lib.attn_paged_decode_num_partitions(64, 16, 4, 16, 0) == 1
+    # 1 sequence x 2 KV heads: 512 tokens halved down to 128, so 1024 tokens
+    # give 8 partitions; 128 tokens stay one
+    assert lib.attn_paged_decode_num_partitions(1, 2, 64, 16, 0) == 8
+    assert lib.attn_paged_decode_num_partitions(1, 2, 8, 16, 0) == 1
+    assert lib.attn_paged_decode_num_partitions(4, 16, 4, 16, 16) == 4
+    assert lib.attn_paged_decode_num_partitions(4, 16, 4, 16, 24) == -INVALID
+    assert lib.attn_paged_decode_num_partitions(4, 0, 4, 16, 0) == -INVALID
+    # (num_seqs, num_query_heads, num_kv_heads, head_size, max_blocks_per_seq, ...)
+    need64 = lib.attn_paged_decode_workspace_size(64, 16, 16, 128, 64, 16, 0)
+    rows = 64 * 16 * 2
+    assert need64 == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert lib.attn_paged_decode_workspace_size(64, 16, 16, 128, 4, 16, 0) == 0
+    need = lib.attn_paged_decode_workspace_size(4, 16, 16, 128, 64, 16, 0)
+    assert need > 0
     assert decode(lib, maxb=64, ws=None, ws_bytes=0) == WORKSPACE
     assert decode(lib, maxb=64, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
     assert decode(lib, maxb=64, ws=FAKE + 16, ws_bytes=need) == WORKSPACE   # not 256-aligned
@@ -149,10 +159,10 @@ def test_decode_noalloc_rejects_what_its_buffer_cannot_hold(lib):
     assert decode_noalloc(lib, query=None) == INVALID
     limit = 64 << 20
     big = dict(num_seqs=256, hq=64, hkv=8, maxb=64, part=16)      # 64 partitions each
-    need = lib.attn_paged_decode_workspace_size(256, 64, 128, 64, 16, 16)
+    need = lib.attn_paged_decode_workspace_size(256, 64, 8, 128, 64, 16, 16)
     assert need > limit
     assert decode_noalloc(lib, **big) == WORKSPACE
-    fits = lib.attn_paged_decode_workspace_size(256, 64, 128, 64, 16, 256)   # 4 partitions
+    fits = lib.attn_paged_decode_workspace_size(256, 64, 8, 128, 64, 16, 256)   # 4 partitions
     assert 0 < fits <= limit
 
 

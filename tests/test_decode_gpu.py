@@ -70,6 +70,47 @@ def test_sharp_attention_over_a_long_context():
     full_check(inp, "sharp, 64-token partitions", partition_size=64)
 
 
+@pytest.mark.parametrize("dtype,head_size,partition_size",
+                         [("bf16", 128, 0), ("fp16", 128, 0), ("bf16", 128, 64), ("bf16", 256, 32)])
+def test_identical_value_rows_return_that_row(dtype, head_size, partition_size):
+    # Every token of a KV head carries the same value row u, so out =
+    # (sum_j w_j) u / sum_j w_j for any weights.  The weights that multiply V
+    # are rounded to 16 bits; when the row sum adds up those same rounded
+    # weights, the quotient is u up to fp32 rounding and rounds back to u bit
+    # for bit (a sum of the unrounded weights misses by up to one unit in the
+    # last place).  Contexts from 1 token to several partitions.
+    lens = [1, 15, 16, 17, 100, 333, 700, 0]
+    inp = gen.decode_inputs(8, 700, 8, 2, head_size, seed=61, dtype=dtype, seq_lens=lens)
+    inp["query"] = (inp["query"].float() * 4).to(inp["query"].dtype)   # weights spread over 2^10 and more
+    u = inp["v_cache"][0, :, :, 0].clone()                              # [Hkv, D]
+    inp["v_cache"] = u[None, :, :, None].expand_as(inp["v_cache"]).contiguous()
+    print(f"[decode] identical V rows {dtype} D={head_size} partition {partition_size}", flush=True)
+    out = run(inp, partition_size).cpu()
+    for s, n in enumerate(lens):
+        for hq in range(8):
+            want = u[hq // 4] if n > 0 else torch.zeros_like(u[0])
+            assert torch.equal(out[s, hq], want), (s, n, hq)
+
+
+def test_automatic_partitions_for_few_long_contexts():
+    # Few workgroups (sequence x KV head) and long contexts: the library's
+    # own choice (partition_size 0) splits the context into 128-token
+    # partitions, which must match the explicit 128-token split bit for bit
+    # and the oracle to the parity bar.
+    from softmax_attention_flashattention_amd import attn_paged_decode_num_partitions
+    cases = [(1, 16, 2, 128, "bf16", [1000]), (2, 8, 1, 128, "bf16", [3000, 77]),
+             (3, 16, 2, 256, "fp16", [700, 1, 513])]
+    for i, (n, hq, hkv, D, dtype, lens) in enumerate(cases):
+        inp = gen.decode_inputs(n, max(lens), hq, hkv, D, seed=71 + i, dtype=dtype, seq_lens=lens)
+        maxb = inp["block_tables"].shape[1]
+        parts = attn_paged_decode_num_partitions(n, hkv, maxb, 16)
+        assert parts == (maxb * 16 + 127) // 128, (parts, maxb)
+        what = f"{n} seqs x {hkv} KV heads, contexts {lens}, D {D} {dtype}: {parts} automatic partitions"
+        _, auto = full_check(inp, what)
+        explicit = run(inp, 128)
+        assert torch.equal(auto, explicit), what
+
+
 def test_one_token_context_returns_value_row_exactly():
     inp = gen.decode_inputs(8, 1, 4, 2, 128, seed=7)
     per = gen.permute_blocks(inp, seed=8)

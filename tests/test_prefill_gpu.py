@@ -159,14 +159,20 @@ def test_single_key_returns_value_rows_exactly(D):
     assert torch.equal(out[50:].cpu(), v[1:2].expand(3, 4, D))
 
 
-@pytest.mark.parametrize("D", [72, 128])
-def test_identical_value_rows_return_that_row(D):
-    inp = gen.prefill_inputs([300], 2, D, seed=33)
-    inp["v"] = inp["v"][7:8].expand(300, 2, D).contiguous()
-    out = f64(run(inp))
-    row = f64(inp["v"][7])
-    # within one bf16 ulp of the row
-    assert np.all(np.abs(out - row[None]) <= 2.0 ** -7 * np.abs(row[None]) + 1e-30)
+@pytest.mark.parametrize("D,dtype,S", [(72, "bf16", 300), (128, "bf16", 300), (72, "fp16", 300),
+                                         (128, "fp16", 300), (72, "bf16", 2100), (128, "bf16", 2100)])
+def test_identical_value_rows_return_that_row(D, dtype, S):
+    # All keys carry the same value row u, so out = (sum_j p_j) u / sum_j p_j.
+    # The row sum adds up the same 16-bit weights that multiply V, so the
+    # quotient is u up to fp32 rounding and rounds back to u bit for bit.
+    # 2100 tokens x 2 heads is a small grid: every item runs as key ranges
+    # merged by log-sum-exp.
+    inp = gen.prefill_inputs([S], 2, D, seed=33, dtype=dtype)
+    inp["q"] = (inp["q"].float() * 4).to(inp["q"].dtype)   # weights spread over 2^10 and more
+    inp["v"] = inp["v"][7:8].expand(S, 2, D).contiguous()
+    print(f"[prefill] identical V rows D={D} {dtype} S={S}", flush=True)
+    out = run(inp).cpu()
+    assert torch.equal(out, inp["v"])
 
 
 @pytest.mark.parametrize("D", [72, 128])

@@ -54,7 +54,7 @@ def compare(inp, partition_size, what):
 def test_two_calls_in_a_row_the_second_smaller():
     big = gen.decode_inputs(64, 1000, 16, 4, 128, seed=201,
                             seq_lens=[1000, 17, 0, 640, 999, 1, 512, 513] * 8)
-    assert binding.attn_paged_decode_num_partitions(63, 16, 64) == 16
+    assert binding.attn_paged_decode_num_partitions(64, 4, 63, 16, 64) == 16
     compare(big, 64, "64 seqs x ctx <= 1000, 16 partitions of 64 tokens")
     small = gen.decode_inputs(8, 300, 8, 8, 256, seed=202, dtype="fp16",
                               seq_lens=[300, 33, 1, 0, 288, 100, 17, 256])
