@@ -6,8 +6,9 @@ this module.  It wraps ``chunk_oracle.c`` (plain C, double precision, OpenMP)
 through ctypes and shares nothing with the GPU library.
 
 Shapes follow the operator page (atrex-bench "chunk_delta_rule_output" #004,
-Reference Implementation): ``batch, tokens, num_q_heads, key_dim = q.shape``,
-``num_heads, value_dim = v.shape[2], v.shape[3]``; ``h`` is
+Reference Implementation): ``q`` and ``k`` are ``[batch, tokens, num_q_heads,
+key_dim]``, ``v`` is ``[batch, tokens, num_heads, value_dim]`` (its last two
+dimensions give the value-head count and the value width), ``h`` is
 ``[batch, num_chunks, num_heads, key_dim, value_dim]`` and ``g`` is float32
 ``[batch, tokens, num_heads]``.  The default scale is ``key_dim ** -0.5``.
 Inputs are CPU tensors (q, k, v, h in bfloat16 or float16, g in float32);

@@ -5,13 +5,14 @@ this module.  It wraps ``attn_oracle.c`` (plain C, double precision, OpenMP)
 through ctypes and shares nothing with the GPU library: not its kernels, not
 its header, not its Python binding.
 
-Shapes are derived from the tensors the way the operator pages do it
-(atrex-bench "attention_forward" #001 and "paged_attention_decode" #024,
-Reference Implementation):
+Sizes come from the tensor shapes under the shape conventions of the
+operator pages (atrex-bench "attention_forward" #001 and
+"paged_attention_decode" #024, Reference Implementation):
 
 * prefill: ``q``, ``k``, ``v`` are packed ``[tokens, num_heads, head_dim]``;
-* decode: ``num_seqs, num_query_heads, head_size = query.shape``,
-  ``num_kv_heads = v_cache.shape[1]``, ``block_size = v_cache.shape[3]``.
+* decode: the query is ``[num_seqs, num_query_heads, head_size]``, and the
+  value cache's second and fourth dimensions are the KV-head count and the
+  block size.
 
 The default scale is ``head_dim ** -0.5``, the default of the
 scaled-dot-product routine both pages call.  Inputs are CPU tensors in

@@ -1,13 +1,14 @@
 """ctypes binding of libattn (``include/attn.h``): argument marshalling only.
 
-Each function here has the name of the C entry point it calls.  It derives the
-scalar sizes from tensor shapes the way the operator pages do
-(atrex-bench "attention_forward" #001 and "paged_attention_decode" #024,
-Reference Implementation: ``num_seqs, num_query_heads, head_size =
-query.shape``, ``num_kv_heads = v_cache.shape[1]``, ``block_size =
-v_cache.shape[3]``), allocates outputs and the decode workspace with torch,
-passes raw device pointers and torch's current HIP stream, and raises on a
-non-OK status.  Every step of the computation runs in the HIP library; if the
+Each function here has the name of the C entry point it calls.  It takes the
+scalar sizes from the tensor shapes under the shape conventions of the
+operator pages (atrex-bench "attention_forward" #001 and
+"paged_attention_decode" #024, Reference Implementation): the three
+dimensions of the decode query are the sequence count, the query-head count
+and the head size, and the value cache's second and fourth dimensions are the
+KV-head count and the block size.  It allocates outputs and the decode
+workspace with torch, passes raw device pointers and torch's current HIP
+stream, and raises on a non-OK status.  Every step of the computation runs in the HIP library; if the
 library is missing the call fails loudly -- there is no fallback.
 """
 import ctypes
