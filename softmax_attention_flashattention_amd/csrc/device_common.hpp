@@ -33,6 +33,13 @@ struct Bf16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
+    // 16x16x32 MFMA: D = A * B + C (A: 16 rows x 32 k, B: 32 k x 16 cols); lane l
+    // holds row / col l % 16 and k 8 (l / 16) .. +7 of A / B, and rows
+    // 4 (l / 16) .. +3 of column l % 16 of C
+    static __device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
     // acc + a.lo * b.lo + a.hi * b.hi for two packed pairs (v_dot2_f32_bf16)
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -62,6 +69,10 @@ struct Fp16 {
     }
     static __device__ __forceinline__ f32x16 mfma32(s16x8 a, s16x8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {

@@ -39,9 +39,10 @@
 // as well (where c * -inf would be NaN).
 //
 // The QK^T contraction is padded to 80 (five k-steps of 16; the K pad columns
-// are zero) and the V^T row blocks to 96; column 72 of the V tile holds 1.0,
-// so row 72 of O^T accumulates the row sum of the 16-bit P that actually
-// multiplied V (the padding does useful work instead of a VALU sum).
+// are zero).  O^T is two 32-row blocks (dims 0-63) on 32x32x16 MFMAs and a
+// 16-row tail (dims 64-79) on 16x16x32 MFMAs; column 72 of the V tile holds
+// 1.0, so tail row 8 (dim 72) accumulates the row sum of the 16-bit P that
+// actually multiplied V (the padding does useful work instead of a VALU sum).
 #pragma once
 
 #include <type_traits>
@@ -69,7 +70,7 @@ struct PrefillParams {
 template <int D> struct PrefillShape;
 template <> struct PrefillShape<72> {
     static constexpr int KSTEPS = 5;    // 72 padded to 80
-    static constexpr int DBLK = 3;      // 72 padded to 96
+    static constexpr int DBLK = 2;      // 32-row O^T blocks (dims 0-63); dims 64-79 form a 16-row tail
     static constexpr int KPITCH = 88;   // 176 B: 16 lanes reading one column hit distinct banks
     static constexpr int VPITCH = 96;   // 192 B: rows 48 banks apart
     static constexpr int ONES_COL = 72;
@@ -275,6 +276,11 @@ void prefill_fwd_kernel(PrefillParams p)
     int v_rd[S::DBLK];
 #pragma unroll
     for (int db = 0; db < S::DBLK; ++db) v_rd[db] = tr_row * VP + 32 * db + tr_col;
+    // The tail's A operand (16x16x32: dim 64 + l % 16, keys of group l / 16
+    // of a 32-key chunk) by the same transposed reads over columns 64-79:
+    // group g takes keys 16 (g % 2) + 4 (g / 2) .. +3 and the same +8, the
+    // keys its lanes hold in the tail's B operand (the regrouped P in pv).
+    const int v_rd_tail = (16 * (g16 & 1) + 4 * (g16 >> 1) + ((lane & 15) >> 2)) * VP + 64 + 4 * (lane & 3);
 
     // S^T = K Q^T for the two 32-key blocks of a tile
     auto compute_s = [&](auto par, f32x16 (&sacc)[2]) {
@@ -309,29 +315,79 @@ void prefill_fwd_kernel(PrefillParams p)
     for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    // O^T tail, dims 64-79: elements 4 h .. 4 h + 3 of otail hold the 16x16
+    // block of queries 16 h .. 16 h + 15 (lane l: query 16 h + l % 16, dims
+    // 64 + 4 (l / 16) .. +3); elements 8-15 are unused (two separate 4-wide
+    // accumulators made the register allocator copy every accumulator between
+    // the loop's two step bodies)
+    f32x16 otail;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) otail[r] = 0.f;
 
-    // O^T += V^T P^T.  kc outer, db inner: consecutive MFMAs are independent.
-    // Between the MFMAs runs `slice(j)`, a piece of VALU work (the row max of
-    // the next tile).
+    // O^T += V^T P^T over the tile's two 32-key chunks m.  Per chunk: the
+    // 32-row blocks take 16-key steps kc = 2m, 2m + 1 (P words 4 kc .. +3 as
+    // their B operand); the tail takes the whole chunk in one 16x16x32 MFMA
+    // per 16 queries (half the MFMA work of a third 32-row block).  The
+    // tail's B operand (P^T of 16 queries, 8 keys in each 16-lane row) is
+    // the same P regrouped by one v_permlane16_swap per word pair.  Lane rows
+    // 0 and 2 hold queries 0-15 and rows 1 and 3 queries 16-31; for queries
+    // 0-15, rows 0 and 2 keep their step-2m words and rows 1 and 3 take the
+    // step-(2m+1) words of rows 0 and 2; for queries 16-31, rows 1 and 3 keep
+    // their step-(2m+1) words and rows 0 and 2 take the step-2m words of rows
+    // 1 and 3.  Order per chunk (consecutive MFMAs independent): big(2m, 0),
+    // big(2m, 1), big(2m+1, 0), big(2m+1, 1), tail(queries 0-15),
+    // tail(queries 16-31); the swap goes in place once the chunk's big MFMAs
+    // have read its words.  Between the MFMAs runs `slice(j)`, a piece of
+    // VALU work (the row max of the next tile).
     auto pv = [&](auto par, const uint32_t (&pw)[16], auto &&slice) {
-        constexpr int NPV = 4 * S::DBLK;   // MFMAs, j = kc * DBLK + db
-        constexpr int PD = 3;              // V^T operands read this many MFMAs ahead
+        constexpr int NPV = 12;   // MFMA slots j: 6 per chunk
+        constexpr int NOP = 10;   // V^T operands o: per chunk 4 big (o % 5 < 4) and the tail's
+        constexpr int PD = 3;     // operands read this many ahead
         const uint16_t *vt = vbuf(par);
-        auto vop = [&](int j) {
-            const uint16_t *base = vt + 16 * (j / S::DBLK) * VP + v_rd[j % S::DBLK];
+        auto vop = [&](int o) {
+            const int m = o / 5, oo = o % 5;
+            const uint16_t *base = oo < 4 ? vt + 16 * (2 * m + oo / 2) * VP + v_rd[oo % 2]
+                                          : vt + 32 * m * VP + v_rd_tail;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base));
             const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + 8 * VP));
             return s16x8{lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         };
+        // the operand of slot j (slots 4 and 5 of a chunk share the tail's)
+        auto op_of = [](int j) { return 5 * (j / 6) + (j % 6 < 4 ? j % 6 : 4); };
         s16x8 a[PD + 1];
 #pragma unroll
-        for (int j = 0; j < PD; ++j) a[j] = vop(j);
+        for (int o = 0; o < PD; ++o) a[o] = vop(o);
+        uint32_t tb[2][4];
 #pragma unroll
         for (int j = 0; j < NPV; ++j) {
-            if (j + PD < NPV) a[(j + PD) % (PD + 1)] = vop(j + PD);
-            const int kc = j / S::DBLK, db = j % S::DBLK;
-            const uint4 w4 = {pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]};
-            oacc[db] = T::mfma32(a[j % (PD + 1)], __builtin_bit_cast(s16x8, w4), oacc[db]);
+            const int m = j / 6, jj = j % 6;
+            // read ahead up to operand op_of(j) + PD (the ring slot it takes
+            // was last used PD + 1 operands back)
+            const int o_lo = j == 0 ? PD : op_of(j - 1) + PD + 1;
+            const int o_hi = op_of(j) + PD + 1 < NOP ? op_of(j) + PD + 1 : NOP;
+#pragma unroll
+            for (int o = o_lo; o < o_hi; ++o) a[o % (PD + 1)] = vop(o);
+            const s16x8 &av = a[op_of(j) % (PD + 1)];
+            if (jj >= 4) {
+                const int h = jj - 4;
+                if (!h) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const auto r = __builtin_amdgcn_permlane16_swap(pw[8 * m + w], pw[8 * m + 4 + w], false, false);
+                        tb[0][w] = r[0];
+                        tb[1][w] = r[1];
+                    }
+                }
+                const uint4 w4 = {tb[h][0], tb[h][1], tb[h][2], tb[h][3]};
+                f32x4 c4 = {otail[4 * h], otail[4 * h + 1], otail[4 * h + 2], otail[4 * h + 3]};
+                c4 = T::mfma16(av, __builtin_bit_cast(s16x8, w4), c4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) otail[4 * h + r] = c4[r];
+            } else {
+                const int kc = 2 * m + jj / 2, db = jj % 2;
+                const uint4 w4 = {pw[4 * kc], pw[4 * kc + 1], pw[4 * kc + 2], pw[4 * kc + 3]};
+                oacc[db] = T::mfma32(av, __builtin_bit_cast(s16x8, w4), oacc[db]);
+            }
             slice(j);
         }
     };
@@ -365,6 +421,13 @@ void prefill_fwd_kernel(PrefillParams p)
             for (int db = 0; db < S::DBLK; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            // the tail's columns are queries l % 16 and 16 + l % 16
+            const float a_lo = __shfl(alpha, lane & 15, 64), a_hi = __shfl(alpha, 16 + (lane & 15), 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                otail[r] *= a_lo;
+                otail[4 + r] *= a_hi;
+            }
         }
     };
 
@@ -461,8 +524,8 @@ void prefill_fwd_kernel(PrefillParams p)
         // first PV MFMAs (before the MFMAs that use them), and the row max of
         // the next tile along all PV MFMAs.
         constexpr int NA = 8;   // 8 measured 0.4% faster than 10, 6 and 12 slower
-        constexpr int NPV = 4 * S::DBLK;
-        constexpr int NB = 2 * S::DBLK;   // PV MFMAs carrying the late pairs
+        constexpr int NPV = 12;   // PV MFMA slots
+        constexpr int NB = 6;     // PV MFMAs carrying the late pairs (chunk 1 starts at slot 6)
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int ks = i >> 1, kb2 = i & 1;
@@ -483,7 +546,8 @@ void prefill_fwd_kernel(PrefillParams p)
         // may hand the buffers over.  The first KD operands of K(t+2), which
         // the next step starts with, are then read while those MFMAs run.
         constexpr int BAR_AT = 3;
-        static_assert(BAR_AT <= 4, "the barrier must follow the last V^T operand read (PD = 3 ahead)");
+        // (pv issues its last V^T read, operand 9, at slot 6)
+        static_assert(NPV - BAR_AT >= 6, "the barrier must follow the last V^T operand read");
         pv(par, pw, [&](int j) {
             if (j < NB) exp_pairs(NA + ((16 - NA) * j) / NB, NA + ((16 - NA) * (j + 1)) / NB);
             mx = max_part(nxt, j, NPV, mx);
@@ -515,10 +579,14 @@ void prefill_fwd_kernel(PrefillParams p)
     if (t + 2 < t1) step(t + 2, P0{}, P1{}, sa, sb, Masked{});
 
     // ---- epilogue: normalise, round to 16 bits, store rows inside the segment
-    // the row sum: row 72 of O^T = block 2, register 4, lanes 0..31
-    const float lv = oacc[2][4];
-    const float other = swap_halves(lv);
-    const float l_tot = hi ? other : lv;
+    // the row sum: dim 72 = tail row 8, in lanes 32-47: otail element 0 for
+    // query l % 16, element 4 for query 16 + l % 16
+    const float l_lo = __shfl(otail[0], 32 + (l32 & 15), 64);
+    const float l_hi = __shfl(otail[4], 32 + (l32 & 15), 64);
+    const float l_tot = l32 < 16 ? l_lo : l_hi;
+    // dims 64-71 of the tail: lanes 0-31, 4 dims (64 + 4 (l / 16)) for each of
+    // queries c0 = l % 16 and c1 = 16 + l % 16 of this wave
+    const int c0 = lane & 15, c1 = 16 + (lane & 15), dt = 64 + 4 * (g16 & 1);
     if (nparts > 1) {
         // a key range of a split item: unnormalised O^T, running max and row
         // sum to the workspace; prefill_merge_kernel combines the ranges
@@ -538,6 +606,16 @@ void prefill_fwd_kernel(PrefillParams p)
                 }
             if (hi == 0) *reinterpret_cast<float2 *>(p.ws_ml + (slot * BM + row) * 2) = make_float2(m_run, l_tot);
         }
+        if (lane < 32) {
+            const int64_t slot = static_cast<int64_t>(w - p.whole_work) * nparts + part;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 32 * wave + (h ? c1 : c0);
+                if (q0 + row < Sq)
+                    *reinterpret_cast<float4 *>(p.ws_o + (slot * BM + row) * D + dt) =
+                        make_float4(otail[4 * h], otail[4 * h + 1], otail[4 * h + 2], otail[4 * h + 3]);
+            }
+        }
         return;
     }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -555,6 +633,20 @@ void prefill_fwd_kernel(PrefillParams p)
                     *reinterpret_cast<uint2 *>(orow + d) = w2;
                 }
             }
+    }
+    const float inv0 = __shfl(inv, c0, 64), inv1 = __shfl(inv, c1, 64);
+    if (lane < 32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = q0 + 32 * wave + (h ? c1 : c0);
+            const float iv = h ? inv1 : inv0;
+            if (q < Sq) {
+                uint2 w2;
+                w2.x = pack2<T>(otail[4 * h] * iv, otail[4 * h + 1] * iv);
+                w2.y = pack2<T>(otail[4 * h + 2] * iv, otail[4 * h + 3] * iv);
+                *reinterpret_cast<uint2 *>(p.out + (qa + q) * rs + head * D + dt) = w2;
+            }
+        }
     }
 }
 
