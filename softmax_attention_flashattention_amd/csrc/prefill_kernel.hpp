@@ -523,7 +523,7 @@ void prefill_fwd_kernel(PrefillParams p)
         // 0 .. NA-1 ride along the NS S MFMAs, the last 16 - NA along the
         // first PV MFMAs (before the MFMAs that use them), and the row max of
         // the next tile along all PV MFMAs.
-        constexpr int NA = 8;   // 8 measured 0.4% faster than 10, 6 and 12 slower
+        constexpr int NA = 10;  // one pair per S MFMA: 0.6% faster than 8 and 6 (interleaved A/B)
         constexpr int NPV = 12;   // PV MFMA slots
         constexpr int NB = 6;     // PV MFMAs carrying the late pairs (chunk 1 starts at slot 6)
 #pragma unroll
