@@ -10,6 +10,7 @@
 #include "chunk_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "prefill_d128_kernel.hpp"
+#include "prefill_d72_kernel.hpp"
 #include "prefill_kernel.hpp"
 
 // Device-side scratch of attn_paged_decode_noalloc: the per-partition
@@ -39,6 +40,20 @@ int launch_prefill(const attn::PrefillParams &p, int64_t grid, hipStream_t strea
     if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
     hipLaunchKernelGGL((attn::prefill_merge_kernel<D, BM, T>),
                        dim3(static_cast<unsigned>((p.total_work - p.whole_work) * attn::merge_blocks<D, BM>())),
+                       dim3(attn::kMergeThreads), 0, stream, p);
+    return launch_status();
+}
+
+template <typename T>
+int launch_prefill_d72(const attn::PrefillParams &p, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn::prefill_fwd_d72_kernel<T>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::kD72Threads), 0, stream, p);
+    int rc = launch_status();
+    if (rc != ATTN_OK || p.split_parts == 1 || p.total_work == p.whole_work) return rc;
+    hipLaunchKernelGGL((attn::prefill_merge_kernel<72, attn::kD72BM, T>),
+                       dim3(static_cast<unsigned>((p.total_work - p.whole_work) *
+                                                  attn::merge_blocks<72, attn::kD72BM>())),
                        dim3(attn::kMergeThreads), 0, stream, p);
     return launch_status();
 }
@@ -75,32 +90,44 @@ int prefill_slots()
     return kernel_slots(attn::prefill_fwd_kernel<D, attn::Bf16, W>, attn::prefill_threads(W));
 }
 
-// Waves per workgroup for a call, and the resulting work items and slots.
-// head_dim 128 runs prefill_fwd_d128_kernel: 4 waves of 64 query rows (256
-// rows per item).  head_dim 72 takes 8 waves (256 query rows) when those
-// items fill every slot at least once; smaller grids keep 4 (the shorter
-// Shapes rows ran up to 30% slower with 8: fewer, longer work items).
+// The kernel for a call, and the resulting work items and slots.  head_dim
+// 128 runs prefill_fwd_d128_kernel (4 waves of 64 query rows, 256 rows per
+// item).  head_dim 72 runs prefill_fwd_d72_kernel (also 4 waves of 64 rows)
+// when its items fill every slot at least once; smaller grids run
+// prefill_fwd_kernel with 8 waves of 32 rows (256 rows per item, one
+// workgroup per CU) when those items fill the device, else with 4 waves (128
+// rows): the shorter Shapes rows ran up to 30% slower on fewer, longer items.
+enum PrefillKind { kPrefill32x4, kPrefill32x8, kPrefillD72, kPrefillD128 };
 struct PrefillShapeChoice {
-    int waves = 4, bm = 128, slots = 0;
+    PrefillKind kind = kPrefill32x4;
+    int bm = 128, slots = 0;
     int64_t qtiles = 0, work = 0;
 };
 
 PrefillShapeChoice choose_prefill(int64_t num_seqs, int64_t max_seqlen_q, int64_t num_heads, int head_dim)
 {
     PrefillShapeChoice c;
+    const int64_t work256 = num_seqs * num_heads * ((max_seqlen_q + 255) / 256);
     if (head_dim == 72) {
+        const int slots64 = kernel_slots(attn::prefill_fwd_d72_kernel<attn::Bf16>, attn::kD72Threads);
         const int slots8 = prefill_slots<72, 8>();
-        const int64_t work8 = num_seqs * num_heads * ((max_seqlen_q + 255) / 256);
-        if (slots8 > 0 && work8 >= slots8) {
-            c.waves = 8;
+        if (slots64 > 0 && work256 >= slots64) {
+            c.kind = kPrefillD72;
+            c.slots = slots64;
+            c.bm = attn::kD72BM;
+        } else if (slots8 > 0 && work256 >= slots8) {
+            c.kind = kPrefill32x8;
             c.slots = slots8;
+            c.bm = attn::prefill_bm(8);
         } else {
             c.slots = prefill_slots<72, 4>();
+            c.bm = attn::prefill_bm(4);
         }
     } else {
+        c.kind = kPrefillD128;
         c.slots = kernel_slots(attn::prefill_fwd_d128_kernel<attn::Bf16>, attn::kD128Threads);
+        c.bm = attn::kD128BM;
     }
-    c.bm = head_dim == 128 ? attn::kD128BM : attn::prefill_bm(c.waves);
     c.qtiles = (max_seqlen_q + c.bm - 1) / c.bm;
     c.work = num_seqs * num_heads * c.qtiles;
     return c;
@@ -347,14 +374,17 @@ int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *
     p.negate_q = scale < 0.f ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    if (head_dim == 128)
-        return dtype == ATTN_DTYPE_BF16 ? launch_prefill_d128<attn::Bf16>(p, pl.grid, s)
-                                        : launch_prefill_d128<attn::Fp16>(p, pl.grid, s);
-    if (c.waves == 8)
-        return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16, 8>(p, pl.grid, s)
-                                        : launch_prefill<72, attn::Fp16, 8>(p, pl.grid, s);
-    return dtype == ATTN_DTYPE_BF16 ? launch_prefill<72, attn::Bf16, 4>(p, pl.grid, s)
-                                    : launch_prefill<72, attn::Fp16, 4>(p, pl.grid, s);
+    const bool bf = dtype == ATTN_DTYPE_BF16;
+    switch (c.kind) {
+    case kPrefillD128:
+        return bf ? launch_prefill_d128<attn::Bf16>(p, pl.grid, s) : launch_prefill_d128<attn::Fp16>(p, pl.grid, s);
+    case kPrefillD72:
+        return bf ? launch_prefill_d72<attn::Bf16>(p, pl.grid, s) : launch_prefill_d72<attn::Fp16>(p, pl.grid, s);
+    case kPrefill32x8:
+        return bf ? launch_prefill<72, attn::Bf16, 8>(p, pl.grid, s) : launch_prefill<72, attn::Fp16, 8>(p, pl.grid, s);
+    default:
+        return bf ? launch_prefill<72, attn::Bf16, 4>(p, pl.grid, s) : launch_prefill<72, attn::Fp16, 4>(p, pl.grid, s);
+    }
 }
 
 int32_t attn_paged_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,

@@ -271,8 +271,8 @@ def test_workload_s276_h4_d72_full():
 
 
 def test_workload_s8136_h16_d72_every_element():
-    # 16 heads x 8136 rows at head_dim 72 (the 8-wave workgroups), every
-    # output element against the oracle
+    # 16 heads x 8136 rows at head_dim 72 (one wave of 512 items of 256 rows,
+    # 64 query rows per wave), every output element against the oracle
     name = "prefill_s8136_h16_d72"
     inp = gen.workload_inputs(name)
     print(f"[prefill] workload {name}: every element", flush=True)
@@ -301,8 +301,8 @@ def test_workload_s16742_h32_d128_every_work_item():
 
 
 def test_workload_s65556_h16_d72_every_work_item():
-    # 257 tiles of 256 rows x 16 heads = 4112 items on the 8-wave path (256
-    # resident workgroups): 16 full waves, and the last 16 items (head 15)
+    # 257 tiles of 256 rows x 16 heads = 4112 items of 64-row waves (512
+    # resident workgroups): 8 full waves, and the last 16 items (head 15)
     # split into key ranges.  One row from every 128-row half of every item.
     every_item_check("prefill_s65556_h16_d72", 128, seed=13)
 
@@ -373,10 +373,9 @@ def test_varlen_batch_with_split_tail():
 
 @pytest.mark.parametrize("D", [72, 128])
 def test_split_last_wave_matches_whole_items(D):
-    # 516 heads x 300 rows: one or two full waves of workgroups (one query
-    # tile of 128 rows at head_dim 72, two of 256 at 128) plus a few items,
-    # which the library splits into key ranges (5 key tiles of 64 rows, 10
-    # of 32, over up to 8 ranges) and merges
+    # 516 heads x 300 rows: two query tiles of 256 rows, so two full waves of
+    # 512 workgroups plus 8 items, which the library splits into key ranges
+    # (10 key tiles of 32 rows over up to 8 ranges) and merges
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
     inp = gen.prefill_inputs([300], 516, D, seed=77)
     assert attn_varlen_fwd_workspace_size(1, 300, 516, D) > 0
@@ -400,9 +399,10 @@ def test_split_last_wave_matches_whole_items(D):
 
 
 def test_eight_wave_items_with_a_split_last_wave():
-    # head_dim 72, 33024 tokens x 2 heads: 258 work items of 256 query rows
-    # (8-wave workgroups, chosen when the items fill the device once) -- one
-    # full wave plus two items, which are split into key ranges and merged
+    # head_dim 72, 33024 tokens x 2 heads: 258 work items of 256 query rows,
+    # too few for the 64-row waves' 512 slots, so 8-wave workgroups of 32-row
+    # waves (256 resident) -- one full wave plus two items, which are split
+    # into key ranges and merged
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
     S, H, D = 33024, 2, 72
     inp = gen.prefill_inputs([S], H, D, seed=79)
@@ -429,8 +429,8 @@ def test_eight_wave_items_with_a_split_last_wave():
 
 @pytest.mark.parametrize("D", [72, 128])
 def test_fp16_on_a_device_filling_grid(D):
-    # 8136 tokens x 16 heads in fp16: at head_dim 72 this grid takes the
-    # 8-wave workgroups, at 128 exactly one wave of 512 items of 256 rows
+    # 8136 tokens x 16 heads in fp16: exactly one wave of 512 items of 256
+    # rows, with 64 query rows per wave at either head_dim
     S, H = 8136, 16
     inp = gen.prefill_inputs([S], H, D, seed=81, dtype="fp16")
     out = run(inp)
@@ -511,3 +511,86 @@ def test_small_grid_split_with_uneven_key_lengths():
     ref_abs = oracle.varlen_fwd(inp["q"], inp["k"], inp["v"].abs(), inp["cu_seqlens_q"],
                                 inp["cu_seqlens_k"])
     check(f64(out), ref, "uneven keys", ref_abs=ref_abs)
+
+
+# ---- head_dim 72 with 64 query rows per wave (prefill_fwd_d72_kernel): the
+# library takes it when the 256-row work items fill the device's 512
+# resident workgroups at least once, so these cases use enough heads for that.
+
+def wide_heads(max_len):
+    """Heads that make at least 512 work items of 256 query rows."""
+    return -(-512 // -(-max_len // 256))
+
+
+@pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 255, 256, 257, 300])
+def test_d72_64_row_waves_single_sequence_lengths(S):
+    H = wide_heads(S)
+    full_check(gen.prefill_inputs([S], H, 72, seed=600 + S), f"64-row waves S={S} H={H}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_d72_64_row_waves_varlen_batch(dtype):
+    # an empty query segment, S_q != S_k, a sequence with no keys, ragged tiles
+    inp = gen.prefill_inputs([5, 0, 300, 64, 129, 1], 48, 72, seed=607, dtype=dtype,
+                             seq_lens_k=[7, 3, 250, 0, 129, 200])
+    full_check(inp, f"64-row waves varlen {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_d72_64_row_waves_zero_and_negative_scale(scale):
+    inp = gen.prefill_inputs([100, 37, 200], 176, 72, seed=651, seq_lens_k=[70, 129, 5])
+    scaled_check(inp, scale, f"64-row waves scale {scale}")
+
+
+def test_d72_64_row_waves_sharp_attention():
+    # rising maxima: the rescale branch on many tiles
+    inp = gen.prefill_inputs([700, 90], 96, 72, seed=655)
+    inp["q"] = (inp["q"].float() * 32).to(torch.bfloat16)
+    k = inp["k"].clone()
+    norms = k[:700].float().norm(dim=2).sum(dim=1)
+    k[:700] = k[:700][torch.argsort(norms)]
+    inp["k"] = k
+    full_check(inp, "64-row waves sharp")
+
+
+@pytest.mark.parametrize("Sk", [1, 17, 38, 300])
+def test_d72_64_row_waves_never_read_past_the_keys(Sk):
+    H = 256
+    inp = gen.prefill_inputs([20, 300], H, 72, seed=690 + Sk, seq_lens_k=[64, Sk])
+    tk = inp["k"].shape[0]
+    d = to_gpu(inp)
+    kb = torch.full((tk + 80, H, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((tk + 80, H, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb[:tk] = d["k"]
+    vb[:tk] = d["v"]
+    out = torch.full_like(d["q"], float("nan"))
+    attn_varlen_fwd(d["q"], kb[:tk], vb[:tk], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=inp["max_seqlen_q"], out=out)
+    torch.cuda.synchronize()
+    ref, ref_abs = refs(inp)
+    check(f64(out), ref, f"64-row waves, NaN past the keys Sk={Sk}", ref_abs=ref_abs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_d72_64_row_waves_identical_value_rows(dtype):
+    S, H = 300, 256
+    inp = gen.prefill_inputs([S], H, 72, seed=633, dtype=dtype)
+    inp["q"] = (inp["q"].float() * 4).to(inp["q"].dtype)
+    inp["v"] = inp["v"][7:8].expand(S, H, 72).contiguous()
+    out = run(inp).cpu()
+    assert torch.equal(out, inp["v"])
+
+
+def test_d72_64_row_waves_rows_outside_segments_untouched():
+    inp = gen.prefill_inputs([40, 300], 256, 72, seed=609)
+    pad = torch.zeros(30, 256, 72, dtype=torch.bfloat16)
+    inp["q"] = torch.cat([inp["q"], pad])
+    d = to_gpu(inp)
+    out = torch.full_like(d["q"], SENTINEL)
+    attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=300, out=out)
+    torch.cuda.synchronize()
+    o = f64(out)
+    assert np.all(o[340:] == SENTINEL)
+    ref, ref_abs = refs(inp)
+    check(o[:340], ref[:340], "64-row waves sentinel", ref_abs=ref_abs[:340])
