@@ -164,52 +164,59 @@ def chunk_bytes(inp):
 
 def oracle_prefill_sample(name, budget_s):
     """The oracle's whole-workload prefill entry point on the first n query
-    rows of head 0 of a prefill workload (one query segment of n rows against
-    all of the sequence's keys: the definition for those rows, computed the
-    way a whole run computes them), n sized to about budget_s seconds."""
+    rows of the first h heads of a prefill workload (a query segment of n rows
+    against all of the sequence's keys: the definition for those rows,
+    computed the way a whole run computes them), sized to about budget_s
+    seconds: rows of head 0 first, then whole heads."""
     import oracle
     import torch
     from softmax_attention_flashattention_amd import inputs as gen
     inp = gen.workload_inputs(name)
     S, H, D = inp["q"].shape
-    k, v = inp["k"][:, :1].contiguous(), inp["v"][:, :1].contiguous()
 
-    def run(n):
-        q = inp["q"][:n, :1].contiguous()
+    def run(n, h):
+        q = inp["q"][:n, :h].contiguous()
+        k, v = inp["k"][:, :h].contiguous(), inp["v"][:, :h].contiguous()
         cu_q = torch.tensor([0, n], dtype=torch.int32)
         t0 = time.perf_counter()
         oracle.varlen_fwd(q, k, v, cu_q, inp["cu_seqlens_k"])
         return time.perf_counter() - t0
 
-    n = min(S, max(oracle.num_threads(), 16))
-    t = run(n)
-    runs = [(n, t)]
+    n, h = min(S, max(oracle.num_threads(), 16)), 1
+    t = run(n, h)
+    runs = [(n, h, t)]
     for _ in range(2):
-        n = int(min(S, max(n, n * budget_s / max(t, 1e-3))))
-        t = run(n)
-        runs.append((n, t))
+        target = int(n * h * budget_s / max(t, 1e-3))
+        if target <= S:
+            n, h = max(n, target), 1
+        else:
+            n, h = S, int(min(H, max(1, target // S)))
+        t = run(n, h)
+        runs.append((n, h, t))
     # A whole run gathers each head's keys and values once, then computes
     # its rows: per head, time = a + b x rows.  a and b from the smallest and
     # largest sample; the whole workload takes H (a + b S).
-    (n1, t1), (n2, t2) = runs[0], runs[-1]
-    b = (t2 - t1) / (n2 - n1) if n2 > n1 else t2 / n2
-    a = max(0.0, t2 - b * n2)
-    b = (t2 - a) / n2
+    (n1, h1, t1), (n2, h2, t2) = runs[0], runs[-1]
+    b = (t2 / h2 - t1 / h1) / (n2 - n1) if n2 > n1 else t2 / (h2 * n2)
+    a = max(0.0, t2 / h2 - b * n2)
+    b = (t2 / h2 - a) / n2
     flops = prefill_flops(inp)
-    return {"mode": "sample", "rows": n, "heads": 1, "of_row_heads": S * H, "keys": S,
-            "seconds": round(t, 3), "tflops": flops * n / (S * H) / t / 1e12,
+    return {"mode": "sample", "rows": n, "heads": h, "of_row_heads": S * H, "keys": S,
+            "seconds": round(t, 3), "tflops": flops * n * h / (S * H) / t / 1e12,
             "extrapolated_full_seconds": round(H * (a + b * S), 1),
             "extrapolation": f"per head {a:.3g} s for the keys + {b:.3g} s per row, times {H} heads"}
 
 
 def cpu_baseline(budget_s):
     """The oracle, as it stands, on a bounded sample of the step's prefill
-    workload: its first query rows of head 0, each against all keys."""
+    workload: its first query rows (of head 0, then of whole heads), each
+    against all keys."""
     import oracle
     smp = oracle_prefill_sample(PREFILL, budget_s)
     return {"value": smp["tflops"], "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the first {smp['rows']} query rows of head 0 of {PREFILL} (of "
-                      f"{smp['of_row_heads']} (row, head) pairs), each against all {smp['keys']} keys, "
+            "sample": f"the first {smp['rows']} query rows of the first {smp['heads']} head(s) of "
+                      f"{PREFILL} (of {smp['of_row_heads']} (row, head) pairs), each against all "
+                      f"{smp['keys']} keys, "
                       f"through the oracle's whole-workload prefill entry point, float64, "
                       f"{smp['seconds']:.1f} s",
             "extrapolated_full_seconds": smp["extrapolated_full_seconds"],

@@ -398,13 +398,16 @@ def test_split_last_wave_matches_whole_items(D):
     check(f64(split), f64(whole), f"split vs whole D={D}")
 
 
-def test_eight_wave_items_with_a_split_last_wave():
-    # head_dim 72, 33024 tokens x 2 heads: 258 work items of 256 query rows,
-    # too few for the 64-row waves' 512 slots, so 8-wave workgroups of 32-row
-    # waves (256 resident) -- one full wave plus two items, which are split
-    # into key ranges and merged
+@pytest.mark.parametrize("S,H", [(5888, 12), (33024, 2)])
+def test_head_dim_72_items_with_a_split_last_wave(S, H):
+    # 5888 tokens x 12 heads: 276 work items of 256 query rows, enough to fill
+    # the 256 resident 8-wave workgroups of 32-row waves (too few for the
+    # 64-row waves' 512, and the sequences are short), so one full wave plus
+    # 20 items, which are split into key ranges and merged.  33024 tokens x 2
+    # heads: 258 items of 64-row waves (long sequences take them on any grid),
+    # a more-than-half-full single wave whose items are split into ranges.
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
-    S, H, D = 33024, 2, 72
+    D = 72
     inp = gen.prefill_inputs([S], H, D, seed=79)
     assert attn_varlen_fwd_workspace_size(1, S, H, D) > 0
     d = to_gpu(inp)
@@ -422,9 +425,9 @@ def test_eight_wave_items_with_a_split_last_wave():
     ref = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"], *args)
     ref_abs = oracle.varlen_fwd_rows(inp["q"], inp["k"], inp["v"].abs(), *args)
     idx = (torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda())
-    check(f64(split[idx]), ref, "8-wave split", ref_abs=ref_abs)
-    check(f64(whole[idx]), ref, "8-wave whole", ref_abs=ref_abs)
-    check(f64(split), f64(whole), "8-wave split vs whole")
+    check(f64(split[idx]), ref, f"{S}x{H} split", ref_abs=ref_abs)
+    check(f64(whole[idx]), ref, f"{S}x{H} whole", ref_abs=ref_abs)
+    check(f64(split), f64(whole), f"{S}x{H} split vs whole")
 
 
 @pytest.mark.parametrize("D", [72, 128])
