@@ -44,12 +44,13 @@ CHUNK = "chunk_t14807_h32_hq16"
 # the sources each kernel's counter figures depend on
 KERNEL_SOURCES = {
     "prefill_fwd_d128_kernel": ["prefill_d128_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
+    "prefill_fwd_d72_kernel": ["prefill_d72_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "prefill_fwd_kernel": ["prefill_kernel.hpp", "device_common.hpp"],
     "decode_partition_kernel": ["decode_kernel.hpp", "device_common.hpp"],
     "chunk_delta_out_kernel": ["chunk_kernel.hpp", "device_common.hpp"],
 }
-ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp",
-               "device_common.hpp"]
+ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_d72_kernel.hpp", "prefill_kernel.hpp", "decode_kernel.hpp",
+               "chunk_kernel.hpp", "device_common.hpp"]
 # the page rows ("attention_forward" Shapes table) of the prefill workloads
 WORKLOAD_PAGE_ROWS = {"prefill_s276_h4_d72": 11, "prefill_s8136_h16_d72": 4,
                       "prefill_s16742_h32_d128": 9, "prefill_s65556_h16_d72": 8}
@@ -58,11 +59,17 @@ PREFILL_CONFIGS = ["prefill_s276_h4_d72", "prefill_s8136_h16_d72", "prefill_s167
                    "prefill_s65556_h16_d72"]
 
 
-def prefill_kernel(head_dim):
-    """(name prefix, label) of the kernel that runs a prefill at this head_dim."""
+def prefill_kernel(head_dim, seq_len, num_heads):
+    """(name prefix, label) of the kernel the library runs for a one-sequence
+    prefill of these sizes on a 256-CU device: the choice the library makes
+    (choose_prefill in csrc/attn_api.hip), restated for the label only."""
     if head_dim == 128:
         return "prefill_fwd_d128_kernel", "prefill_fwd_d128_kernel<bf16>"
-    return "prefill_fwd_kernel", f"prefill_fwd_kernel<{head_dim}, bf16>"
+    items256 = num_heads * -(-seq_len // 256)
+    if items256 >= 512 or seq_len >= 6144:
+        return "prefill_fwd_d72_kernel", "prefill_fwd_d72_kernel<bf16>"
+    waves = 8 if items256 >= 256 else 4
+    return "prefill_fwd_kernel", f"prefill_fwd_kernel<72, bf16, {waves}>"
 
 
 class ClockSampler:
@@ -694,7 +701,7 @@ def main():
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / reps
             rate = xf / (ms * 1e-3) / 1e12
-            entry = {"head_dim": D, "kernel": prefill_kernel(D)[1], "flops_per_launch": xf,
+            entry = {"head_dim": D, "kernel": prefill_kernel(D, S, H)[1], "flops_per_launch": xf,
                      "launches": reps, "avg_launch_us": round(ms * 1e3, 2), "achieved": round(rate, 1),
                      "unit": "TFLOP/s", "frac": round(rate / PEAK_BF16_TFLOPS, 4)}
             if ms < 0.2:
@@ -719,7 +726,8 @@ def main():
         return profiled_traffic(prefix, kernel_source_hash(KERNEL_SOURCES[prefix]))
 
     src_hash = kernel_source_hash(ALL_SOURCES)
-    pre_prefix, pre_label = prefill_kernel(int(p_host["q"].shape[2]))
+    pre_prefix, pre_label = prefill_kernel(int(p_host["q"].shape[2]), int(p_host["max_seqlen_q"]),
+                                           int(p_host["q"].shape[1]))
     pre_traffic = traffic(pre_prefix) if p_name == PREFILL else None
     dec_traffic = traffic("decode_partition_kernel")
     chunk_traffic = traffic("chunk_delta_out_kernel")
