@@ -1,6 +1,8 @@
-// prefill_kernel.hpp -- non-causal varlen prefill attention for gfx950,
-// head_dim 72 (head_dim 128 runs prefill_d128_kernel.hpp); also the
-// parameter block and the key-range merge kernel both prefill kernels share.
+// prefill_kernel.hpp -- non-causal varlen prefill attention for gfx950 at
+// head_dim 72 with 32 query rows per wave, for grids that the 64-row kernel
+// of prefill_d72_kernel.hpp runs slower (head_dim 128 runs
+// prefill_d128_kernel.hpp); also the parameter block and the key-range merge
+// kernel that all prefill kernels share.
 //
 // Computes, per sequence and head, out = softmax(scale * Q K^T) V (the
 // operator of the atrex-bench page "attention_forward" #001, Reference
@@ -468,7 +470,7 @@ void prefill_fwd_kernel(PrefillParams p)
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(k_head + static_cast<int64_t>(t + 2) * BN * rs, tile_bytes(t + 2));
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_head + static_cast<int64_t>(t + 1) * BN * rs, tile_bytes(t + 1));
         // DMA instruction n of this wave's DJK + DJV goes after S MFMA
-        // floor(n NS / (DJK + DJV)) (every other MFMA for head_dim 128)
+        // floor(n NS / (DJK + DJV))
         auto dma_slot = [&](int mfma) {
             constexpr int ND = DJK + DJV;
 #pragma unroll
