@@ -123,10 +123,17 @@ class ClockSampler:
 
 
 def kernel_source_hash(names):
+    """Hash of the code of kernel source files, comments and blank space left
+    out (so that an edited comment keeps the counter figures taken on the
+    same code)."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "softmax_attention_flashattention_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "softmax_attention_flashattention_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
