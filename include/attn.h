@@ -98,7 +98,7 @@ typedef enum attn_dtype {
  *
  * num_seqs == 0, max_seqlen_q == 0 or total_q == 0 is a valid no-op.
  */
-int attn_varlen_fwd(const void *q, const void *k, const void *v,
+attn_status attn_varlen_fwd(const void *q, const void *k, const void *v,
                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                     int32_t num_seqs, int32_t max_seqlen_q,
                     int64_t total_q, int64_t total_k,
@@ -149,7 +149,7 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q,
  *
  * num_seqs == 0 is a valid no-op.
  */
-int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+attn_status attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *seq_lens,
                       int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
                       int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
@@ -181,7 +181,7 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
  *    written by the same call.
  */
 #define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
-int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
+attn_status attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
                               const int32_t *block_tables, const int32_t *seq_lens,
                               int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
@@ -234,7 +234,7 @@ size_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_query_head
  *
  * batch == 0 or tokens == 0 is a valid no-op (pointers may then be NULL).
  */
-int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h,
+attn_status attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h,
                          const float *g, int32_t batch, int32_t tokens, int32_t num_q_heads,
                          int32_t num_heads, int32_t key_dim, int32_t value_dim,
                          int32_t chunk_size, float scale, int32_t dtype, void *out,

@@ -324,11 +324,11 @@ size_t attn_varlen_fwd_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, in
     return plan_prefill(c.work, c.slots, c.bm, head_dim, key_tiles).ws_bytes;
 }
 
-int attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
-                    const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
-                    int64_t total_q, int64_t total_k, int32_t num_heads, int32_t head_dim,
-                    float scale, int32_t dtype, void *workspace, size_t workspace_bytes, void *out,
-                    void *stream)
+static int attn_varlen_fwd_impl(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                                const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                int64_t total_q, int64_t total_k, int32_t num_heads, int32_t head_dim,
+                                float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                                void *out, void *stream)
 {
     if (num_seqs < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || num_heads <= 0 ||
         head_dim <= 0)
@@ -495,12 +495,12 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
 
 extern "C" {
 
-int attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
-                      const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
-                      int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
-                      int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                      int32_t dtype, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                      void *out, void *stream)
+static int attn_paged_decode_impl(const void *query, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                                  int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  float scale, int32_t dtype, int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *out, void *stream)
 {
     const int rc = check_decode_args(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                      num_query_heads, num_kv_heads, head_size, block_size,
@@ -512,12 +512,12 @@ int attn_paged_decode(const void *query, const void *k_cache, const void *v_cach
                                workspace, workspace_bytes, out, stream);
 }
 
-int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
-                              const int32_t *block_tables, const int32_t *seq_lens,
-                              int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
-                              int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
-                              int64_t num_blocks, float scale, int32_t dtype,
-                              int32_t partition_size, void *out, void *stream)
+static int attn_paged_decode_noalloc_impl(const void *query, const void *k_cache, const void *v_cache,
+                                          const int32_t *block_tables, const int32_t *seq_lens,
+                                          int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                                          int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                          int64_t num_blocks, float scale, int32_t dtype,
+                                          int32_t partition_size, void *out, void *stream)
 {
     const int rc = check_decode_args(query, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                      num_query_heads, num_kv_heads, head_size, block_size,
@@ -538,10 +538,10 @@ int attn_paged_decode_noalloc(const void *query, const void *k_cache, const void
                                out, stream);
 }
 
-int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h, const float *g,
-                         int32_t batch, int32_t tokens, int32_t num_q_heads, int32_t num_heads,
-                         int32_t key_dim, int32_t value_dim, int32_t chunk_size, float scale,
-                         int32_t dtype, void *out, void *stream)
+static int attn_chunk_delta_out_impl(const void *q, const void *k, const void *v, const void *h,
+                                     const float *g, int32_t batch, int32_t tokens, int32_t num_q_heads,
+                                     int32_t num_heads, int32_t key_dim, int32_t value_dim,
+                                     int32_t chunk_size, float scale, int32_t dtype, void *out, void *stream)
 {
     if (batch < 0 || tokens < 0 || num_q_heads <= 0 || num_heads <= 0 || key_dim <= 0 ||
         value_dim <= 0 || chunk_size <= 0)
@@ -585,6 +585,58 @@ int attn_chunk_delta_out(const void *q, const void *k, const void *v, const void
         hipLaunchKernelGGL((attn::chunk_delta_out_kernel<attn::Fp16>), dim3(static_cast<unsigned>(grid)),
                            dim3(attn::kChunkThreads), 0, s, p);
     return launch_status();
+}
+
+
+// The entry points proper: the implementations above return attn_status values as int.
+attn_status attn_varlen_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                            int64_t total_q, int64_t total_k, int32_t num_heads, int32_t head_dim,
+                            float scale, int32_t dtype, void *workspace, size_t workspace_bytes, void *out,
+                            void *stream)
+{
+    return static_cast<attn_status>(attn_varlen_fwd_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs,
+                                                         max_seqlen_q, total_q, total_k, num_heads,
+                                                         head_dim, scale, dtype, workspace, workspace_bytes,
+                                                         out, stream));
+}
+
+attn_status attn_paged_decode(const void *query, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *seq_lens, int32_t num_seqs,
+                              int32_t num_query_heads, int32_t num_kv_heads, int32_t head_size,
+                              int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                              float scale, int32_t dtype, int32_t partition_size, void *workspace,
+                              size_t workspace_bytes, void *out, void *stream)
+{
+    return static_cast<attn_status>(attn_paged_decode_impl(query, k_cache, v_cache, block_tables, seq_lens,
+                                                           num_seqs, num_query_heads, num_kv_heads,
+                                                           head_size, block_size, max_blocks_per_seq,
+                                                           num_blocks, scale, dtype, partition_size,
+                                                           workspace, workspace_bytes, out, stream));
+}
+
+attn_status attn_paged_decode_noalloc(const void *query, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_tables, const int32_t *seq_lens,
+                                      int32_t num_seqs, int32_t num_query_heads, int32_t num_kv_heads,
+                                      int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, float scale, int32_t dtype,
+                                      int32_t partition_size, void *out, void *stream)
+{
+    return static_cast<attn_status>(attn_paged_decode_noalloc_impl(query, k_cache, v_cache, block_tables,
+                                                                   seq_lens, num_seqs, num_query_heads,
+                                                                   num_kv_heads, head_size, block_size,
+                                                                   max_blocks_per_seq, num_blocks, scale,
+                                                                   dtype, partition_size, out, stream));
+}
+
+attn_status attn_chunk_delta_out(const void *q, const void *k, const void *v, const void *h, const float *g,
+                                 int32_t batch, int32_t tokens, int32_t num_q_heads, int32_t num_heads,
+                                 int32_t key_dim, int32_t value_dim, int32_t chunk_size, float scale,
+                                 int32_t dtype, void *out, void *stream)
+{
+    return static_cast<attn_status>(attn_chunk_delta_out_impl(q, k, v, h, g, batch, tokens, num_q_heads,
+                                                              num_heads, key_dim, value_dim, chunk_size,
+                                                              scale, dtype, out, stream));
 }
 
 }  // extern "C"
