@@ -50,15 +50,16 @@ def test_prefill_split_and_merge_replays(D):
         f"prefill 2024 x 4 heads, D={D}")
 
 
-def test_prefill_eight_wave_split_replays():
-    # head_dim 72 on a device-filling grid: 8-wave workgroups, with the two
-    # items past the first full wave split into key ranges and merged
-    inp = gen.prefill_inputs([33024], 2, 72, seed=95)
+@pytest.mark.parametrize("S,H", [(5888, 12), (33024, 2)])
+def test_prefill_head_dim_72_split_replays(S, H):
+    # head_dim 72 with a split last wave, merged: 5888 x 12 heads on 8-wave
+    # workgroups of 32-row waves, 33024 x 2 heads on 64-row waves
+    inp = gen.prefill_inputs([S], H, 72, seed=95)
     d = to_gpu(inp)
     replay_matches_eager(
         lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
-                                max_seqlen_q=33024),
-        "prefill 33024 x 2 heads, D=72, 8 waves")
+                                max_seqlen_q=S),
+        f"prefill {S} x {H} heads, D=72")
 
 
 def test_prefill_varlen_batch_replays():
