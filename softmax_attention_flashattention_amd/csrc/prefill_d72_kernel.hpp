@@ -317,9 +317,9 @@ void prefill_fwd_d72_kernel(PrefillParams p)
         s16x8 va = vop(vt, 0);
 #pragma unroll
         for (int j = 0; j < 6; ++j) {
-            const s16x8 a = va;
-            if (j < 4) va = vop(vt, j + 1);   // j = 3 reads the tail's operand
             if (j < 4) {
+                const s16x8 a = va;
+                va = vop(vt, j + 1);   // slot 3 reads the tail's operand, used by slots 4 and 5
                 const int kc = j >> 1, db = j & 1;
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
@@ -348,7 +348,6 @@ void prefill_fwd_d72_kernel(PrefillParams p)
                     for (int r = 0; r < 4; ++r) otail[8 * qb + 4 * h + r] = c4[r];
                 }
             }
-            (void)a;
             slice(j);
             __builtin_amdgcn_sched_barrier(0);
         }
