@@ -34,9 +34,11 @@
  *    indices so that they never read or write outside the buffers described
  *    by the size arguments.
  *  - The only mutable global state is attn_paged_decode_noalloc's device
- *    buffer (one per GPU) and its looked-up address; other calls on different
- *    streams may run concurrently as long as their `out`/`workspace` buffers
- *    differ.
+ *    buffer (one per GPU) and its looked-up address, and facts about each
+ *    device the launch plans use (compute units, resident workgroups per
+ *    kernel), queried once on a device's first call and kept; other calls on
+ *    different streams may run concurrently as long as their
+ *    `out`/`workspace` buffers differ.
  */
 #ifndef LIBATTN_ATTN_H
 #define LIBATTN_ATTN_H

@@ -73,21 +73,42 @@ int launch_prefill_d128(const attn::PrefillParams &p, int64_t grid, hipStream_t 
 }
 
 // Work items that fit the device at once: compute units x resident
-// workgroups per unit of `kernel` (0 when the runtime cannot tell, e.g. no
-// device).
+// workgroups per unit of `kernel` (0 when the runtime cannot tell).
 template <typename K>
-int kernel_slots(K kernel, int threads)
+int kernel_slots(int dev, K kernel, int threads)
 {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
     return e == hipSuccess ? cus * per_cu : 0;
 }
-template <int D, int W>
-int prefill_slots()
+
+// What the launch plans need to know of a device, queried once per device
+// (the answers are fixed for the process; the queries cost host time on
+// every call otherwise).  All zero when there is no current device.
+struct DeviceShape {
+    int cus = 0;        // compute units
+    int slots_d128 = 0, slots_d72 = 0, slots_32x8 = 0, slots_32x4 = 0;
+};
+constexpr int kMaxShapeDevices = 64;
+std::once_flag g_shape_once[kMaxShapeDevices];
+DeviceShape g_shape[kMaxShapeDevices];
+
+const DeviceShape &device_shape()
 {
-    return kernel_slots(attn::prefill_fwd_kernel<D, attn::Bf16, W>, attn::prefill_threads(W));
+    static const DeviceShape none;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxShapeDevices) return none;
+    std::call_once(g_shape_once[dev], [dev] {
+        DeviceShape d;
+        if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
+        d.slots_d128 = kernel_slots(dev, attn::prefill_fwd_d128_kernel<attn::Bf16>, attn::kD128Threads);
+        d.slots_d72 = kernel_slots(dev, attn::prefill_fwd_d72_kernel<attn::Bf16>, attn::kD72Threads);
+        d.slots_32x8 = kernel_slots(dev, attn::prefill_fwd_kernel<72, attn::Bf16, 8>, attn::prefill_threads(8));
+        d.slots_32x4 = kernel_slots(dev, attn::prefill_fwd_kernel<72, attn::Bf16, 4>, attn::prefill_threads(4));
+        g_shape[dev] = d;
+    });
+    return g_shape[dev];
 }
 
 // The kernel for a call, and the resulting work items and slots.  head_dim
@@ -111,10 +132,11 @@ struct PrefillShapeChoice {
 PrefillShapeChoice choose_prefill(int64_t num_seqs, int64_t max_seqlen_q, int64_t num_heads, int head_dim)
 {
     PrefillShapeChoice c;
+    const DeviceShape &ds = device_shape();
     const int64_t work256 = num_seqs * num_heads * ((max_seqlen_q + 255) / 256);
     if (head_dim == 72) {
-        const int slots64 = kernel_slots(attn::prefill_fwd_d72_kernel<attn::Bf16>, attn::kD72Threads);
-        const int slots8 = prefill_slots<72, 8>();
+        const int slots64 = ds.slots_d72;
+        const int slots8 = ds.slots_32x8;
         if (slots64 > 0 && (work256 >= slots64 || max_seqlen_q >= kD72LongRows)) {
             c.kind = kPrefillD72;
             c.slots = slots64;
@@ -124,12 +146,12 @@ PrefillShapeChoice choose_prefill(int64_t num_seqs, int64_t max_seqlen_q, int64_
             c.slots = slots8;
             c.bm = attn::prefill_bm(8);
         } else {
-            c.slots = prefill_slots<72, 4>();
+            c.slots = ds.slots_32x4;
             c.bm = attn::prefill_bm(4);
         }
     } else {
         c.kind = kPrefillD128;
-        c.slots = kernel_slots(attn::prefill_fwd_d128_kernel<attn::Bf16>, attn::kD128Threads);
+        c.slots = ds.slots_d128;
         c.bm = attn::kD128BM;
     }
     c.qtiles = (max_seqlen_q + c.bm - 1) / c.bm;
@@ -237,11 +259,8 @@ int dispatch_decode(const attn::DecodeParams &p, int head_size, int64_t grid, hi
 // Compute units of the current device (256 when the runtime cannot tell).
 int device_cus()
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
+    const int cus = device_shape().cus;
+    return cus > 0 ? cus : 256;
 }
 
 // Tokens per context partition.  Left to the library (partition_size 0):
