@@ -252,8 +252,8 @@ def rows_of_every_tile(S, H, tile, seed, extra_last=True):
     return np.array(rows), np.array(heads)
 
 
-def every_item_check(name, tile, seed):
-    inp = gen.workload_inputs(name)
+def every_item_check(name, tile, seed, inp=None):
+    inp = gen.workload_inputs(name) if inp is None else inp
     S, H, _ = inp["q"].shape
     print(f"[prefill] workload {name}: every work item", flush=True)
     out = run_nan_filled(inp)
@@ -305,6 +305,16 @@ def test_workload_s65556_h16_d72_every_work_item():
     # resident workgroups): 8 full waves, and the last 16 items (head 15)
     # split into key ranges.  One row from every 128-row half of every item.
     every_item_check("prefill_s65556_h16_d72", 128, seed=13)
+
+
+def test_largest_shapes_row_s30793_h32_d128_every_work_item():
+    # the largest head_dim-128 row of the page's Shapes table (row 10):
+    # 121 query tiles of 256 rows x 32 heads = 3872 work items: 7 full waves
+    # of 512 and a last wave of 288 (split into key ranges where that
+    # finishes it sooner); every element written and finite, one row of
+    # every 256-row tile of every head against the oracle
+    inp = gen.prefill_inputs([30793], 32, 128, seed=2010)
+    every_item_check("prefill_s30793_h32_d128", 256, seed=14, inp=inp)
 
 
 @pytest.mark.parametrize("D", [72, 128])
