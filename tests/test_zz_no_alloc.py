@@ -64,3 +64,11 @@ def test_two_calls_in_a_row_the_second_smaller():
 def test_one_partition_uses_no_buffer():
     inp = gen.workload_inputs("decode_b256_ctx64_h16_kv16_d128")
     compare(inp, 0, "256 seqs x ctx 64, one partition")
+
+
+def test_automatic_partitions_use_the_buffer():
+    # partition_size 0 on few long contexts: the library splits them into
+    # 128-token partitions (24 here), whose partials go to the static buffer
+    inp = gen.decode_inputs(2, 3000, 8, 1, 128, seed=203, seq_lens=[3000, 77])
+    assert binding.attn_paged_decode_num_partitions(2, 1, inp["block_tables"].shape[1], 16) == 24
+    compare(inp, 0, "2 seqs x 1 KV head x ctx <= 3000, automatic partitions")
