@@ -607,3 +607,20 @@ def test_d72_64_row_waves_rows_outside_segments_untouched():
     assert np.all(o[340:] == SENTINEL)
     ref, ref_abs = refs(inp)
     check(o[:340], ref[:340], "64-row waves sentinel", ref_abs=ref_abs[:340])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_d72_64_row_waves_random_batches(seed):
+    # random varlen batches (empty segments, S_q != S_k, ragged tiles), bf16
+    # or fp16, a scale of either sign, with enough heads for the 64-row waves;
+    # every element against the oracle
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 7))
+    lq = [int(x) for x in rng.integers(0, 701, n)]
+    lk = [int(x) for x in rng.integers(0, 901, n)]
+    lq[0] = max(lq[0], 1)
+    H = wide_heads(max(lq)) // n + 1
+    dtype = "fp16" if seed % 2 else "bf16"
+    scale = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.05, 0.2))
+    inp = gen.prefill_inputs(lq, H, 72, seed=710 + seed, dtype=dtype, seq_lens_k=lk)
+    scaled_check(inp, scale, f"64-row waves random batch {seed}: {n} seqs, {H} heads, {dtype}, scale {scale:.3f}")
