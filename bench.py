@@ -46,11 +46,12 @@ KERNEL_SOURCES = {
     "prefill_fwd_d128_kernel": ["prefill_d128_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "prefill_fwd_d72_kernel": ["prefill_d72_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "prefill_fwd_kernel": ["prefill_kernel.hpp", "device_common.hpp"],
+    "prefill_fwd_split_kernel": ["prefill_split_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "decode_partition_kernel": ["decode_kernel.hpp", "device_common.hpp"],
     "chunk_delta_out_kernel": ["chunk_kernel.hpp", "device_common.hpp"],
 }
-ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_d72_kernel.hpp", "prefill_kernel.hpp", "decode_kernel.hpp",
-               "chunk_kernel.hpp", "device_common.hpp"]
+ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_d72_kernel.hpp", "prefill_kernel.hpp",
+               "prefill_split_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp", "device_common.hpp"]
 # the page rows ("attention_forward" Shapes table) of the prefill workloads
 WORKLOAD_PAGE_ROWS = {"prefill_s276_h4_d72": 11, "prefill_s8136_h16_d72": 4,
                       "prefill_s16742_h32_d128": 9, "prefill_s65556_h16_d72": 8}
@@ -65,6 +66,8 @@ def prefill_kernel(head_dim, seq_len, num_heads):
     (choose_prefill in csrc/attn_api.hip), restated for the label only."""
     if head_dim == 128:
         return "prefill_fwd_d128_kernel", "prefill_fwd_d128_kernel<bf16>"
+    if num_heads * -(-seq_len // 32) <= 512 and seq_len <= 8192:
+        return "prefill_fwd_split_kernel", "prefill_fwd_split_kernel<bf16, 4>"
     items256 = num_heads * -(-seq_len // 256)
     if items256 >= 512 or seq_len >= 6144:
         return "prefill_fwd_d72_kernel", "prefill_fwd_d72_kernel<bf16>"

@@ -93,7 +93,10 @@ typedef enum attn_dtype {
  *                 holds at once, every item is) whose partial results go
  *                 here and a second kernel merges them.  NULL (or too small)
  *                 runs every item whole: the same result up to rounding,
- *                 only slower in those cases.
+ *                 only slower in those cases.  head_dim-72 grids whose
+ *                 32-row items all fit the device at once (and
+ *                 max_seqlen_q <= 8192) split the keys inside each
+ *                 workgroup instead and use no workspace (size 0).
  *  out            [total_q, num_heads, head_dim], dtype.  Only rows inside a
  *                 query segment are written; a sequence with query rows but
  *                 no key rows gets all-zero rows.  Other rows are untouched.

@@ -40,14 +40,28 @@ def replay_matches_eager(call, what, reps=4):
 
 @pytest.mark.parametrize("D", [72, 128])
 def test_prefill_split_and_merge_replays(D):
-    # 16 query tiles x 4 heads: every item is split into key ranges, so the
-    # graph holds the prefill kernel and the merge kernel
-    inp = gen.prefill_inputs([2024], 4, D, seed=90 + D)
+    # few work items (2024 tokens x 4 heads at head_dim 128, x 10 heads at
+    # 72): every item is split into key ranges, so the graph holds the
+    # prefill kernel and the merge kernel
+    H = 10 if D == 72 else 4
+    inp = gen.prefill_inputs([2024], H, D, seed=90 + D)
     d = to_gpu(inp)
     replay_matches_eager(
         lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
                                 max_seqlen_q=2024),
-        f"prefill 2024 x 4 heads, D={D}")
+        f"prefill 2024 x {H} heads, D={D}")
+
+
+@pytest.mark.parametrize("S,H", [(276, 4), (2024, 4)])
+def test_prefill_key_splitting_workgroups_replay(S, H):
+    # head_dim 72 on a small grid: one kernel whose workgroups merge their
+    # waves' key ranges in LDS
+    inp = gen.prefill_inputs([S], H, 72, seed=97 + S)
+    d = to_gpu(inp)
+    replay_matches_eager(
+        lambda: attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                                max_seqlen_q=S),
+        f"prefill {S} x {H} heads, D=72, key-splitting workgroups")
 
 
 @pytest.mark.parametrize("S,H", [(5888, 12), (33024, 2)])

@@ -166,7 +166,8 @@ def test_identical_value_rows_return_that_row(D, dtype, S):
     # The row sum adds up the same 16-bit weights that multiply V, so the
     # quotient is u up to fp32 rounding and rounds back to u bit for bit.
     # 2100 tokens x 2 heads is a small grid: every item runs as key ranges
-    # merged by log-sum-exp.
+    # merged by log-sum-exp (at head_dim 128 by a second kernel, at 72
+    # inside the key-splitting workgroups).
     inp = gen.prefill_inputs([S], 2, D, seed=33, dtype=dtype)
     inp["q"] = (inp["q"].float() * 4).to(inp["q"].dtype)   # weights spread over 2^10 and more
     inp["v"] = inp["v"][7:8].expand(S, 2, D).contiguous()
@@ -459,11 +460,15 @@ def test_fp16_on_a_device_filling_grid(D):
 
 @pytest.mark.parametrize("D", [72, 128])
 def test_small_grid_splits_every_item(D):
-    # 16 query tiles x 4 heads = 64 items, far fewer than the device holds:
-    # every item is split into key ranges and merged
+    # far fewer work items than the device holds, so every item is split into
+    # key ranges and merged: head_dim 128, 8 query tiles of 256 rows x 4
+    # heads; head_dim 72, 16 tiles of 128 rows x 10 heads (with 4 heads the
+    # 32-row items of the key-splitting workgroups would all fit at once,
+    # and those need no merge)
     from softmax_attention_flashattention_amd import attn_varlen_fwd_workspace_size
-    inp = gen.prefill_inputs([2024], 4, D, seed=78)
-    assert attn_varlen_fwd_workspace_size(1, 2024, 4, D) > 0
+    H = 10 if D == 72 else 4
+    inp = gen.prefill_inputs([2024], H, D, seed=78)
+    assert attn_varlen_fwd_workspace_size(1, 2024, H, D) > 0
     d = to_gpu(inp)
     print(f"[prefill] small grid split D={D}", flush=True)
     split = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
@@ -624,3 +629,112 @@ def test_d72_64_row_waves_random_batches(seed):
     scale = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.05, 0.2))
     inp = gen.prefill_inputs(lq, H, 72, seed=710 + seed, dtype=dtype, seq_lens_k=lk)
     scaled_check(inp, scale, f"64-row waves random batch {seed}: {n} seqs, {H} heads, {dtype}, scale {scale:.3f}")
+
+
+# ---- head_dim 72 on small grids (prefill_fwd_split_kernel): the library
+# takes it when the items of 32 query rows all fit the device at once (512
+# resident workgroups) and max_seqlen_q <= 8192.  Each of a workgroup's 4
+# waves walks a quarter of the key tiles; the quarters are merged in LDS.
+# The short cases earlier in this file (2-3 heads) run here too: they cover
+# wave ranges left empty (fewer than 4 key tiles), sequences without keys,
+# both dtypes, scale 0 and negative scales.
+
+def test_split_kernel_long_single_sequence():
+    # 8192 tokens x 1 head: 256 items whose waves walk 64 key tiles each (the
+    # steady-state loop); every element written, one row of every 32-row
+    # item and the first and last rows against the oracle
+    S = 8192
+    inp = gen.prefill_inputs([S], 1, 72, seed=820)
+    print("[prefill] key-splitting workgroups, 8192 x 1", flush=True)
+    out = run_nan_filled(inp)
+    assert bool(torch.isfinite(out).all())
+    rows, heads = rows_of_every_tile(S, 1, 32, seed=821)
+    ref, ref_abs = oracle_at(inp, rows, heads)
+    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
+    check(got, ref, "8192 x 1: one row per 32-row item", ref_abs=ref_abs)
+
+
+@pytest.mark.parametrize("S", [1024, 1025])
+def test_split_kernel_slot_boundary(S):
+    # 1024 tokens x 16 heads make exactly 512 items of 32 rows (the
+    # key-splitting workgroups); 1025 make 528, which run on the 32-row waves
+    # with key ranges merged by a second kernel.  Both against the oracle on
+    # one row of every 32-row tile of every head.
+    H = 16
+    inp = gen.prefill_inputs([S], H, 72, seed=830 + S)
+    print(f"[prefill] slot boundary {S} x {H}", flush=True)
+    out = run_nan_filled(inp)
+    assert bool(torch.isfinite(out).all())
+    rows, heads = rows_of_every_tile(S, H, 32, seed=S)
+    ref, ref_abs = oracle_at(inp, rows, heads)
+    got = f64(out[torch.from_numpy(rows).cuda(), torch.from_numpy(heads).cuda()])
+    check(got, ref, f"{S} x {H}", ref_abs=ref_abs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_split_kernel_varlen_batch_uneven_ranges(dtype):
+    # sequences whose key counts leave 0-3 of a workgroup's 4 wave ranges
+    # empty, one with no keys, one with no queries, one with far more keys
+    # than queries (long ranges), a negative scale; every element
+    lq = [33, 1, 0, 90, 200, 31]
+    lk = [40, 0, 7, 95, 2100, 3]
+    inp = gen.prefill_inputs(lq, 3, 72, seed=840, dtype=dtype, seq_lens_k=lk)
+    scaled_check(inp, -0.15, f"key-splitting workgroups, uneven ranges, {dtype}")
+
+
+# ---- head_dim 72 on the 32-row waves (prefill_fwd_kernel<72, T, 4>): grids
+# with more than 512 items of 32 rows but fewer than 256 of 256 rows.  These
+# cases use enough heads for that and otherwise mirror the edge cases above.
+
+@pytest.mark.parametrize("S", [257, 300, 511])
+def test_d72_32_row_waves_single_sequence_lengths(S):
+    full_check(gen.prefill_inputs([S], 64, 72, seed=860 + S), f"32-row waves S={S} H=64")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_d72_32_row_waves_varlen_batch(dtype):
+    inp = gen.prefill_inputs([5, 0, 300, 64, 129, 1], 12, 72, seed=867, dtype=dtype,
+                             seq_lens_k=[9, 4, 300, 1, 200, 64])
+    full_check(inp, f"32-row waves varlen {dtype}")
+
+
+@pytest.mark.parametrize("Sk", [1, 17, 38, 300])
+def test_d72_32_row_waves_keys_past_the_segment_are_never_read(Sk):
+    H = 64
+    inp = gen.prefill_inputs([300], H, 72, seed=870 + Sk, seq_lens_k=[Sk])
+    tk = inp["k"].shape[0]
+    d = to_gpu(inp)
+    kb = torch.full((tk + 80, H, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((tk + 80, H, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kb[:tk] = d["k"]
+    vb[:tk] = d["v"]
+    out = torch.full_like(d["q"], float("nan"))
+    attn_varlen_fwd(d["q"], kb[:tk], vb[:tk], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=300, out=out)
+    torch.cuda.synchronize()
+    ref, ref_abs = refs(inp)
+    check(f64(out), ref, f"32-row waves, NaN past the keys Sk={Sk}", ref_abs=ref_abs)
+
+
+def test_d72_32_row_waves_identical_value_rows():
+    S, H = 300, 64
+    inp = gen.prefill_inputs([S], H, 72, seed=875)
+    inp["q"] = (inp["q"].float() * 4).to(inp["q"].dtype)
+    inp["v"] = inp["v"][7:8].expand(S, H, 72).contiguous()
+    out = run(inp).cpu()
+    assert torch.equal(out, inp["v"])
+
+
+def test_d72_32_row_waves_rows_outside_segments_untouched():
+    inp = gen.prefill_inputs([40, 300], 32, 72, seed=877)
+    pad = torch.zeros(30, 32, 72, dtype=torch.bfloat16)
+    inp["q"] = torch.cat([inp["q"], pad])
+    d = to_gpu(inp)
+    out = torch.full_like(d["q"], SENTINEL)
+    attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
+                    max_seqlen_q=300, out=out)
+    torch.cuda.synchronize()
+    o = f64(out)
+    assert np.all(o[340:] == SENTINEL)
+    ref, ref_abs = refs(inp)
+    check(o[:340], ref[:340], "32-row waves sentinel", ref_abs=ref_abs[:340])
