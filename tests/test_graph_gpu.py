@@ -109,3 +109,26 @@ def test_chunk_output_replays():
     replay_matches_eager(
         lambda: attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"]),
         "chunk output 2 x 300 tokens")
+
+
+def test_calls_take_torch_current_stream():
+    # the binding hands the library torch's current stream of the tensors'
+    # device: inside a stream context that stream's handle, outside it the
+    # default one
+    from softmax_attention_flashattention_amd import binding
+    dev = torch.device("cuda", torch.cuda.current_device())
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert (binding._stream(dev).value or 0) == s.cuda_stream
+    assert (binding._stream(dev).value or 0) == torch.cuda.current_stream(dev).cuda_stream
+    # and a call issued inside the context runs on that stream, ordered after
+    # the work already queued there
+    inp = gen.prefill_inputs([300], 2, 72, seed=99)
+    d = to_gpu(inp)
+    eager = attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], max_seqlen_q=300)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        q2 = d["q"].clone()          # queued on s before the call
+        out = attn_varlen_fwd(q2, d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], max_seqlen_q=300)
+    s.synchronize()
+    assert torch.equal(out, eager)
