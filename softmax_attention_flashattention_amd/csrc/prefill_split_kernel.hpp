@@ -128,10 +128,11 @@ void prefill_fwd_split_kernel(PrefillParams p)
     const int ntiles = (Sk + BN - 1) / BN;
     const int ta = (wave_s * ntiles) / W, tb = ((wave_s + 1) * ntiles) / W;
     const int n = tb - ta;
-    // (Nothing in a step branches on the lane or on the tile: a branch would
+    // Nothing in a step branches on the lane or on the tile: a branch would
     // split the step into blocks, and the compiler would then sink the
-    // softmax work past it, away from the MFMAs it is meant to overlap.)
-    // (tiles t < tb hold at least one key; the extent is 0 from tb on)
+    // softmax work past it, away from the MFMAs it is meant to overlap.
+    // Buffer resource of tile t: its rows up to the sequence's last key
+    // (tiles t < tb hold at least one), zero extent from tb on.
     auto tile_rsrc = [&](const uint16_t *head_base, int t) __attribute__((always_inline)) {
         int rows = Sk - t * BN;
         rows = rows < BN ? rows : BN;
