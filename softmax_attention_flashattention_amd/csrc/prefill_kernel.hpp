@@ -1,8 +1,9 @@
 // prefill_kernel.hpp -- non-causal varlen prefill attention for gfx950 at
-// head_dim 72 with 32 query rows per wave, for grids that the 64-row kernel
-// of prefill_d72_kernel.hpp runs slower (head_dim 128 runs
-// prefill_d128_kernel.hpp); also the parameter block and the key-range merge
-// kernel that all prefill kernels share.
+// head_dim 72 with 32 query rows per wave, for the grids between those of
+// the key-splitting workgroups (prefill_split_kernel.hpp, small grids) and
+// those the 64-row kernel of prefill_d72_kernel.hpp runs faster (head_dim 128
+// runs prefill_d128_kernel.hpp); also the parameter block and the key-range
+// merge kernel that all prefill kernels share.
 //
 // Computes, per sequence and head, out = softmax(scale * Q K^T) V (the
 // operator of the atrex-bench page "attention_forward" #001, Reference
