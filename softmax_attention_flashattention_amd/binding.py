@@ -73,7 +73,8 @@ def _load():
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    """A tensor's device address as a plain int (ctypes passes it as void *)."""
+    return t.data_ptr() if t is not None else None
 
 
 # torch's current stream on a device as a raw handle; the private accessor
@@ -81,10 +82,30 @@ def _ptr(t):
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _stream(device):
-    if _raw_stream is not None and device.index is not None:
-        return ctypes.c_void_p(_raw_stream(device.index))
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _stream(dev):
+    """torch's current stream on GPU index `dev`, as an int handle."""
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ok(t, dtype, ndim, dev):
+    """The common case of the checks `_need` spells out, in a few cheap
+    attribute reads: a contiguous tensor of `dtype` with `ndim` dimensions on
+    GPU index `dev`."""
+    return (isinstance(t, torch.Tensor) and t.dtype is dtype and t.dim() == ndim
+            and t.get_device() == dev and t.is_contiguous())
+
+
+def _gpu_index(t):
+    """The GPU index of a 16-bit floating-point tensor, -1 for anything else."""
+    if isinstance(t, torch.Tensor) and t.dtype in _DTYPE:
+        return t.get_device()
+    return -1
+
+
+# attn_varlen_fwd_workspace_size results by (num_seqs, max_seqlen_q, H, D, GPU)
+_ws_sizes = {}
 
 
 def _need(t, name, dtype=None, ndim=None, device=None):
@@ -113,6 +134,16 @@ def attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, num_heads, head_dim):
                                                   int(num_heads), int(head_dim))
 
 
+def _varlen_ws_bytes(num_seqs, max_seqlen_q, H, D, dev):
+    key = (num_seqs, max_seqlen_q, H, D, dev)
+    n = _ws_sizes.get(key)
+    if n is None:
+        if len(_ws_sizes) > 4096:
+            _ws_sizes.clear()
+        n = _ws_sizes[key] = attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, H, D)
+    return n
+
+
 def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scale=None,
                     out=None, workspace=None):
     """Non-causal varlen prefill attention (calls ``attn_varlen_fwd``).
@@ -125,38 +156,45 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
     tensor) defaults to one allocated here of the size the library asks for;
     an empty tensor runs every work item whole.
     """
-    fp16 = (torch.bfloat16, torch.float16)
-    _need(q, "q", fp16, 3)
-    _need(k, "k", q.dtype, 3, device=q.device)
-    _need(v, "v", q.dtype, 3, device=q.device)
-    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, device=q.device)
-    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, device=q.device)
+    dev = _gpu_index(q)
+    dt = q.dtype if dev >= 0 else None
+    if not (dev >= 0 and q.dim() == 3 and q.is_contiguous() and _ok(k, dt, 3, dev)
+            and _ok(v, dt, 3, dev) and _ok(cu_seqlens_q, torch.int32, 1, dev)
+            and _ok(cu_seqlens_k, torch.int32, 1, dev)):
+        fp16 = (torch.bfloat16, torch.float16)   # name the first failing check
+        _need(q, "q", fp16, 3)
+        _need(k, "k", q.dtype, 3, device=q.device)
+        _need(v, "v", q.dtype, 3, device=q.device)
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, device=q.device)
+        _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, device=q.device)
     total_q, H, D = q.shape
-    if k.shape[1:] != (H, D) or v.shape != k.shape:
+    ks = k.shape
+    if ks[1] != H or ks[2] != D or v.shape != ks:
         raise ValueError("k and v must be [total_k, H, D] with q's H and D")
-    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+    n1 = cu_seqlens_q.numel()
+    if cu_seqlens_k.numel() != n1 or n1 < 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries each")
-    num_seqs = cu_seqlens_q.numel() - 1
+    num_seqs = n1 - 1
     if max_seqlen_q is None:
         max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if num_seqs else 0
+    else:
+        max_seqlen_q = int(max_seqlen_q)
     scale = float(D) ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
-    else:
+    elif not _ok(out, dt, 3, dev) or out.shape != q.shape:
         _need(out, "out", q.dtype, 3, device=q.device)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
+        raise ValueError("out must have q's shape")
     if workspace is None:
-        ws_bytes = attn_varlen_fwd_workspace_size(num_seqs, max_seqlen_q, H, D)
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+        ws_len = _varlen_ws_bytes(num_seqs, max_seqlen_q, H, D, dev)
+        ws_ptr = torch.empty(ws_len, dtype=torch.uint8, device=q.device).data_ptr() if ws_len else None
     else:
         _need(workspace, "workspace", device=q.device)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    ws_ptr = _ptr(workspace) if ws_len else None
-    rc = _load().attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
-                                 _ptr(cu_seqlens_k), num_seqs, int(max_seqlen_q), total_q,
-                                 k.shape[0], H, D, scale, _DTYPE[q.dtype], ws_ptr, ws_len,
-                                 _ptr(out), _stream(q.device))
+        ws_len = workspace.numel() * workspace.element_size()
+        ws_ptr = workspace.data_ptr() if ws_len else None
+    rc = _load().attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                 cu_seqlens_k.data_ptr(), num_seqs, max_seqlen_q, total_q, ks[0], H,
+                                 D, scale, _DTYPE[dt], ws_ptr, ws_len, out.data_ptr(), _stream(dev))
     if rc != 0:
         raise AttnError("attn_varlen_fwd", rc)
     return out
@@ -186,13 +224,18 @@ def attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads, he
 
 def _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out):
     """Checks the decode tensors, derives the sizes from their shapes and
-    returns (sizes, scale, out)."""
-    fp16 = (torch.bfloat16, torch.float16)
-    _need(query, "query", fp16, 3)
-    _need(k_cache, "k_cache", query.dtype, 5, device=query.device)
-    _need(v_cache, "v_cache", query.dtype, 4, device=query.device)
-    _need(block_tables, "block_tables", torch.int32, 2, device=query.device)
-    _need(seq_lens, "seq_lens", torch.int32, 1, device=query.device)
+    returns (sizes, scale, out, GPU index)."""
+    dev = _gpu_index(query)
+    dt = query.dtype if dev >= 0 else None
+    if not (dev >= 0 and query.dim() == 3 and query.is_contiguous() and _ok(k_cache, dt, 5, dev)
+            and _ok(v_cache, dt, 4, dev) and _ok(block_tables, torch.int32, 2, dev)
+            and _ok(seq_lens, torch.int32, 1, dev)):
+        fp16 = (torch.bfloat16, torch.float16)   # name the first failing check
+        _need(query, "query", fp16, 3)
+        _need(k_cache, "k_cache", query.dtype, 5, device=query.device)
+        _need(v_cache, "v_cache", query.dtype, 4, device=query.device)
+        _need(block_tables, "block_tables", torch.int32, 2, device=query.device)
+        _need(seq_lens, "seq_lens", torch.int32, 1, device=query.device)
     num_seqs, num_query_heads, head_size = query.shape
     num_kv_heads = v_cache.shape[1]
     block_size = v_cache.shape[3]
@@ -208,12 +251,11 @@ def _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out):
     scale = float(head_size) ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(query)
-    else:
+    elif not _ok(out, dt, 3, dev) or out.shape != query.shape:
         _need(out, "out", query.dtype, 3, device=query.device)
-        if out.shape != query.shape:
-            raise ValueError("out must have query's shape")
+        raise ValueError("out must have query's shape")
     sizes = (num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks)
-    return sizes, scale, out
+    return sizes, scale, out, dev
 
 
 def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=None, out=None,
@@ -227,7 +269,8 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
     choose) sets the split-K granularity; the workspace it needs is
     allocated here unless one is passed.
     """
-    sizes, scale, out = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out)
+    sizes, scale, out, dev = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale,
+                                           out)
     num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
     ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads,
                                                 head_size, maxb, block_size, partition_size)
@@ -240,7 +283,7 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
                                    _ptr(seq_lens), num_seqs, num_query_heads, num_kv_heads,
                                    head_size, block_size, maxb, num_blocks, scale,
                                    _DTYPE[query.dtype], int(partition_size), _ptr(workspace),
-                                   ws_len, _ptr(out), _stream(query.device))
+                                   ws_len, _ptr(out), _stream(dev))
     if rc != 0:
         raise AttnError("attn_paged_decode", rc)
     return out
@@ -256,13 +299,14 @@ def attn_paged_decode_noalloc(query, k_cache, v_cache, block_tables, seq_lens, s
     AttnError(ATTN_ERR_WORKSPACE) when the split needs more than the buffer
     holds.
     """
-    sizes, scale, out = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out)
+    sizes, scale, out, dev = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale,
+                                           out)
     num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
     rc = _load().attn_paged_decode_noalloc(_ptr(query), _ptr(k_cache), _ptr(v_cache),
                                            _ptr(block_tables), _ptr(seq_lens), num_seqs,
                                            num_query_heads, num_kv_heads, head_size, block_size,
                                            maxb, num_blocks, scale, _DTYPE[query.dtype],
-                                           int(partition_size), _ptr(out), _stream(query.device))
+                                           int(partition_size), _ptr(out), _stream(dev))
     if rc != 0:
         raise AttnError("attn_paged_decode_noalloc", rc)
     return out
@@ -278,12 +322,16 @@ def attn_chunk_delta_out(q, k, v, h, g, chunk_size=64, scale=None, out=None):
     = q.shape``, ``num_heads, value_dim = v.shape[2], v.shape[3]``).
     ``scale`` defaults to K**-0.5.  Returns out [B, T, H, V] in v's dtype.
     """
-    fp16 = (torch.bfloat16, torch.float16)
-    _need(q, "q", fp16, 4)
-    _need(k, "k", q.dtype, 4, device=q.device)
-    _need(v, "v", q.dtype, 4, device=q.device)
-    _need(h, "h", q.dtype, 5, device=q.device)
-    _need(g, "g", torch.float32, 3, device=q.device)
+    dev = _gpu_index(q)
+    dt = q.dtype if dev >= 0 else None
+    if not (dev >= 0 and q.dim() == 4 and q.is_contiguous() and _ok(k, dt, 4, dev)
+            and _ok(v, dt, 4, dev) and _ok(h, dt, 5, dev) and _ok(g, torch.float32, 3, dev)):
+        fp16 = (torch.bfloat16, torch.float16)   # name the first failing check
+        _need(q, "q", fp16, 4)
+        _need(k, "k", q.dtype, 4, device=q.device)
+        _need(v, "v", q.dtype, 4, device=q.device)
+        _need(h, "h", q.dtype, 5, device=q.device)
+        _need(g, "g", torch.float32, 3, device=q.device)
     B, T, Hq, K = q.shape
     H, V = v.shape[2], v.shape[3]
     nc = (T + chunk_size - 1) // chunk_size
@@ -294,13 +342,12 @@ def attn_chunk_delta_out(q, k, v, h, g, chunk_size=64, scale=None, out=None):
     scale = float(K) ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(v)
-    else:
+    elif not _ok(out, dt, 4, dev) or out.shape != v.shape:
         _need(out, "out", v.dtype, 4, device=q.device)
-        if out.shape != v.shape:
-            raise ValueError("out must have v's shape")
+        raise ValueError("out must have v's shape")
     rc = _load().attn_chunk_delta_out(_ptr(q), _ptr(k), _ptr(v), _ptr(h), _ptr(g), B, T, Hq, H, K,
-                                      V, int(chunk_size), scale, _DTYPE[q.dtype], _ptr(out),
-                                      _stream(q.device))
+                                      V, int(chunk_size), scale, _DTYPE[dt], _ptr(out),
+                                      _stream(dev))
     if rc != 0:
         raise AttnError("attn_chunk_delta_out", rc)
     return out

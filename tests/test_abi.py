@@ -208,3 +208,31 @@ def test_binding_names_match_the_header():
     import softmax_attention_flashattention_amd as pkg
     for n in declared_functions():
         assert hasattr(pkg, n), f"binding lacks {n}"
+
+
+def test_binding_checks_tensors_before_any_call():
+    # host tensors and non-tensors are refused by the binding with the name
+    # of the offending argument; nothing reaches the library (these run
+    # without a GPU)
+    import torch
+    import softmax_attention_flashattention_amd as pkg
+    q = torch.zeros(8, 2, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="q must be a GPU tensor"):
+        pkg.attn_varlen_fwd(q, q, q, cu, cu, max_seqlen_q=8)
+    with pytest.raises(TypeError, match="q must be a torch.Tensor"):
+        pkg.attn_varlen_fwd(None, q, q, cu, cu, max_seqlen_q=8)
+    query = torch.zeros(2, 4, 128, dtype=torch.float16)
+    kc = torch.zeros(3, 4, 16, 16, 8, dtype=torch.float16)
+    vc = torch.zeros(3, 4, 128, 16, dtype=torch.float16)
+    bt = torch.zeros(2, 1, dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="query must be a GPU tensor"):
+        pkg.attn_paged_decode(query, kc, vc, bt, sl)
+    with pytest.raises(ValueError, match="query must be a GPU tensor"):
+        pkg.attn_paged_decode_noalloc(query, kc, vc, bt, sl)
+    x = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16)
+    h = torch.zeros(1, 1, 2, 128, 128, dtype=torch.bfloat16)
+    g = torch.zeros(1, 64, 2)
+    with pytest.raises(ValueError, match="q must be a GPU tensor"):
+        pkg.attn_chunk_delta_out(x, x, x, h, g)

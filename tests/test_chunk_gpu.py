@@ -139,3 +139,27 @@ def test_largest_workload_sampled_rows():
     ref = ch.chunk_delta_out_rows(x["q"], x["k"], x["v"], x["h"], x["g"], toks, heads)
     A = ch.chunk_delta_out_rows(x["q"], x["k"], x["v"], x["h"], x["g"], toks, heads, absolute=True)
     bar(out[0, toks, heads], ref, A, name)
+
+
+def test_binding_rejects_mismatched_tensors():
+    # the binding refuses, naming the argument, what the kernel could not read
+    # correctly: host memory, another dtype, a strided view, a bad out
+    x = gen.chunk_inputs(1, 128, 2, 2, seed=97)
+    d = to_gpu(x)
+    args = [d["q"], d["k"], d["v"], d["h"], d["g"]]
+    bad = list(args)
+    bad[4] = x["g"]
+    with pytest.raises(ValueError, match="g must be a GPU tensor"):
+        attn_chunk_delta_out(*bad)
+    bad = list(args)
+    bad[4] = d["g"].double()
+    with pytest.raises(TypeError, match="g has dtype"):
+        attn_chunk_delta_out(*bad)
+    bad = list(args)
+    bad[3] = d["h"].transpose(3, 4).contiguous().transpose(3, 4)
+    with pytest.raises(ValueError, match="h must be contiguous"):
+        attn_chunk_delta_out(*bad)
+    with pytest.raises(TypeError, match="out has dtype"):
+        attn_chunk_delta_out(*args, out=d["v"].float())
+    with pytest.raises(ValueError, match="out must have v's shape"):
+        attn_chunk_delta_out(*args, out=d["v"][:, :64].contiguous())

@@ -179,3 +179,27 @@ def test_head_size_256(dtype, S, L, Hq, Hkv, lens):
     full_check(inp, f"D=256 {dtype} {S}x{L} Hq={Hq} Hkv={Hkv}")
     if L > 256:
         full_check(inp, f"D=256 split {dtype}", partition_size=128)
+
+
+def test_binding_rejects_mismatched_tensors():
+    # the binding refuses, naming the argument, what the library could not
+    # read correctly: host memory, another dtype, a strided view, a bad out
+    inp = gen.decode_inputs(2, 40, 4, 2, 128, seed=61)
+    d = to_gpu(inp)
+    args = [d["query"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"]]
+    bad = list(args)
+    bad[2] = inp["v_cache"]
+    with pytest.raises(ValueError, match="v_cache must be a GPU tensor"):
+        attn_paged_decode(*bad)
+    bad = list(args)
+    bad[1] = d["k_cache"].half()
+    with pytest.raises(TypeError, match="k_cache has dtype"):
+        attn_paged_decode(*bad)
+    bad = list(args)
+    bad[3] = d["block_tables"].t().contiguous().t()
+    with pytest.raises(ValueError, match="block_tables must be contiguous"):
+        attn_paged_decode(*bad)
+    with pytest.raises(TypeError, match="out has dtype"):
+        attn_paged_decode(*args, out=d["query"].float())
+    with pytest.raises(ValueError, match="out must have query's shape"):
+        attn_paged_decode(*args, out=d["query"][:1])

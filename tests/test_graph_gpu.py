@@ -116,11 +116,11 @@ def test_calls_take_torch_current_stream():
     # device: inside a stream context that stream's handle, outside it the
     # default one
     from softmax_attention_flashattention_amd import binding
-    dev = torch.device("cuda", torch.cuda.current_device())
+    dev = torch.cuda.current_device()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        assert (binding._stream(dev).value or 0) == s.cuda_stream
-    assert (binding._stream(dev).value or 0) == torch.cuda.current_stream(dev).cuda_stream
+        assert binding._stream(dev) == s.cuda_stream
+    assert binding._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
     # and a call issued inside the context runs on that stream, ordered after
     # the work already queued there
     inp = gen.prefill_inputs([300], 2, 72, seed=99)

@@ -195,6 +195,23 @@ def test_binding_rejects_host_buffers():
     with pytest.raises(ValueError):
         attn_varlen_fwd(d["q"], inp["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"],
                         max_seqlen_q=20)
+    # and of the right type, layout and shape
+    with pytest.raises(TypeError, match="v has dtype"):
+        attn_varlen_fwd(d["q"], d["k"], d["v"].half(), d["cu_seqlens_q"], d["cu_seqlens_k"],
+                        max_seqlen_q=20)
+    with pytest.raises(ValueError, match="k must be contiguous"):
+        kt = d["k"].transpose(0, 1).contiguous().transpose(0, 1)
+        attn_varlen_fwd(d["q"], kt, d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"], max_seqlen_q=20)
+    with pytest.raises(TypeError, match="cu_seqlens_k has dtype"):
+        attn_varlen_fwd(d["q"], d["k"], d["v"], d["cu_seqlens_q"], d["cu_seqlens_k"].long(),
+                        max_seqlen_q=20)
+    with pytest.raises(TypeError, match="out has dtype"):
+        attn_varlen_fwd(*args, max_seqlen_q=20, out=d["q"].float())
+    with pytest.raises(ValueError, match="out must have q's shape"):
+        attn_varlen_fwd(*args, max_seqlen_q=20, out=d["q"][:10])
+    with pytest.raises(ValueError, match="k and v must be"):
+        attn_varlen_fwd(d["q"], d["k"][:, :1].contiguous(), d["v"][:, :1].contiguous(),
+                        d["cu_seqlens_q"], d["cu_seqlens_k"], max_seqlen_q=20)
 
 
 def test_runs_are_bitwise_deterministic():
