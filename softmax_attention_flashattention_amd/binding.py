@@ -104,7 +104,8 @@ def _gpu_index(t):
     return -1
 
 
-# attn_varlen_fwd_workspace_size results by (num_seqs, max_seqlen_q, H, D, GPU)
+# workspace sizes the library reported, by the sizes of the call and the GPU
+# index (5-tuples: prefill, 8-tuples: decode)
 _ws_sizes = {}
 
 
@@ -237,13 +238,10 @@ def _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale, out):
         _need(block_tables, "block_tables", torch.int32, 2, device=query.device)
         _need(seq_lens, "seq_lens", torch.int32, 1, device=query.device)
     num_seqs, num_query_heads, head_size = query.shape
-    num_kv_heads = v_cache.shape[1]
-    block_size = v_cache.shape[3]
-    num_blocks = v_cache.shape[0]
-    x = 16 // query.element_size()
-    if tuple(k_cache.shape) != (num_blocks, num_kv_heads, head_size // x, block_size, x):
+    num_blocks, num_kv_heads, v_dim, block_size = v_cache.shape
+    if k_cache.shape != (num_blocks, num_kv_heads, head_size // 8, block_size, 8):
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_size/8, block_size, 8]")
-    if tuple(v_cache.shape) != (num_blocks, num_kv_heads, head_size, block_size):
+    if v_dim != head_size:
         raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_size, block_size]")
     if block_tables.shape[0] != num_seqs or seq_lens.numel() != num_seqs:
         raise ValueError("block_tables and seq_lens need one row/entry per sequence")
@@ -272,8 +270,13 @@ def attn_paged_decode(query, k_cache, v_cache, block_tables, seq_lens, scale=Non
     sizes, scale, out, dev = _decode_sizes(query, k_cache, v_cache, block_tables, seq_lens, scale,
                                            out)
     num_seqs, num_query_heads, num_kv_heads, head_size, block_size, maxb, num_blocks = sizes
-    ws_bytes = attn_paged_decode_workspace_size(num_seqs, num_query_heads, num_kv_heads,
-                                                head_size, maxb, block_size, partition_size)
+    key = (num_seqs, num_query_heads, num_kv_heads, head_size, maxb, block_size, partition_size, dev)
+    ws_bytes = _ws_sizes.get(key)
+    if ws_bytes is None:
+        if len(_ws_sizes) > 4096:
+            _ws_sizes.clear()
+        ws_bytes = _ws_sizes[key] = attn_paged_decode_workspace_size(
+            num_seqs, num_query_heads, num_kv_heads, head_size, maxb, block_size, partition_size)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
     elif workspace is not None:

@@ -268,10 +268,10 @@ int launch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
 template <typename T, int D>
 int dispatch_decode_g(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
 {
-    if (p.G <= 1) return launch_decode<T, D, 1>(p, grid, stream);
-    if (p.G <= 2) return launch_decode<T, D, 2>(p, grid, stream);
-    if (p.G <= 4) return launch_decode<T, D, 4>(p, grid, stream);
-    if (p.G <= 8) return launch_decode<T, D, 8>(p, grid, stream);
+    if (p.gsub <= 1) return launch_decode<T, D, 1>(p, grid, stream);
+    if (p.gsub <= 2) return launch_decode<T, D, 2>(p, grid, stream);
+    if (p.gsub <= 4) return launch_decode<T, D, 4>(p, grid, stream);
+    if (p.gsub <= 8) return launch_decode<T, D, 8>(p, grid, stream);
     return launch_decode<T, D, 16>(p, grid, stream);
 }
 
@@ -511,9 +511,24 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     const int np = partitions(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size,
                               &part_blocks);
     if (np < 1) return ATTN_ERR_INVALID_ARG;
-    const int64_t grid = static_cast<int64_t>(num_seqs) * num_kv_heads * np;
-    if (grid > INT32_MAX || static_cast<int64_t>(num_seqs) * num_query_heads > INT32_MAX)
+    const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * np;
+    if (units > INT32_MAX || static_cast<int64_t>(num_seqs) * num_query_heads > INT32_MAX)
         return ATTN_ERR_INVALID_ARG;
+    // Fewer (sequence, KV head, partition) units than compute units: deal
+    // the G query heads of each out to up to cus / units workgroups, one
+    // head each where there is room (graph replayed, 1 sequence x 16/2 heads
+    // x 128 tokens at head_size 256: 13.1 -> 4.9 us; 4 x 32/4 x 128: 9.5 ->
+    // 4.1 us; at least 2 heads per workgroup, or at most 4 workgroups per
+    // unit, were slower on every small row measured).
+    int ngroups = 1;
+    const int cus = device_cus();
+    if (G > 1 && units > 0 && units < cus) {
+        const int64_t room = cus / units;
+        ngroups = static_cast<int>(room < G ? room : G);
+    }
+    const int gsub = (G + ngroups - 1) / ngroups;
+    ngroups = (G + gsub - 1) / gsub;
+    const int64_t grid = units * ngroups;
 
     attn::DecodeParams p;
     p.query = static_cast<const uint16_t *>(query);
@@ -542,6 +557,8 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     p.maxb = max_blocks_per_seq;
     p.part_blocks = part_blocks;
     p.num_parts = np;
+    p.gsub = gsub;
+    p.ngroups = ngroups;
     p.scale_log2e = scale * attn::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, head_size, grid, s)

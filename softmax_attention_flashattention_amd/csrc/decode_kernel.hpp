@@ -32,6 +32,12 @@
 // dim-owning lanes through LDS.  At the end the four waves' (max, sum, partial output)
 // are merged through LDS.
 //
+// Few workgroups: when sequences x KV heads x partitions would leave compute
+// units idle, the G query heads of a KV head are dealt to ngroups
+// workgroups of gsub heads each.  Each reads the same K/V chunks (from L2
+// after the first), and the per-block softmax chain of a wave is gsub heads
+// long instead of G; the outputs are disjoint, so nothing is merged.
+//
 // Split-K: a context longer than one partition is split over several
 // workgroups; each writes (running max m in the log2 domain, sum l,
 // unnormalised output o) to the workspace and decode_merge_kernel combines
@@ -56,6 +62,8 @@ struct DecodeParams {
     int num_seqs, Hq, Hkv, G, maxb;
     int part_blocks;  // blocks per partition
     int num_parts;
+    int gsub;         // query heads per workgroup (G when the heads are not dealt out)
+    int ngroups;      // workgroups per (sequence, KV head, partition): ceil(G / gsub)
     float scale_log2e;
 };
 
@@ -76,10 +84,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
     int id = blockIdx.x;
     const int part = id % p.num_parts;
     id /= p.num_parts;
+    const int gg = id % p.ngroups;
+    id /= p.ngroups;
     const int hk = id % p.Hkv;
     const int s = id / p.Hkv;
-    const int G = p.G;
-    const int hq0 = hk * G;
+    // this workgroup's query heads: hq0 .. hq0 + G - 1 (G <= GMAX)
+    const int hq0 = hk * p.G + gg * p.gsub;
+    const int G = p.G - gg * p.gsub < p.gsub ? p.G - gg * p.gsub : p.gsub;
 
     int L = p.seq_lens[s];
     L = L > p.maxb * BS ? p.maxb * BS : L;

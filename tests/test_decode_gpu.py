@@ -203,3 +203,25 @@ def test_binding_rejects_mismatched_tensors():
         attn_paged_decode(*args, out=d["query"].float())
     with pytest.raises(ValueError, match="out must have query's shape"):
         attn_paged_decode(*args, out=d["query"][:1])
+
+
+@pytest.mark.parametrize("S,L,Hq,Hkv,D,dtype", [
+    (85, 100, 5, 1, 128, "bf16"),     # 85 units: G = 5 dealt as 2 + 2 + 1 heads
+    (1, 128, 16, 2, 256, "bf16"),     # 2 units: one query head per workgroup
+    (3, 700, 16, 1, 128, "fp16"),     # split context (18 units) and heads dealt out: 8 x 2
+    (128, 64, 8, 4, 128, "bf16"),     # 512 units fill the device: all 2 heads in one workgroup
+])
+def test_query_heads_dealt_to_workgroups(S, L, Hq, Hkv, D, dtype):
+    # grids with fewer (sequence, KV head, partition) units than compute
+    # units spread each KV head's query heads over several workgroups; every
+    # output row must still come out once, right
+    lens = [L - (7 * i) % max(L // 3, 1) for i in range(S)]
+    inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + L + Hq + D, dtype=dtype, seq_lens=lens)
+    d = to_gpu(inp)
+    out = torch.full_like(d["query"], float("nan"))
+    attn_paged_decode(d["query"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"],
+                      out=out)
+    torch.cuda.synchronize()
+    what = f"decode {S} x {L} Hq {Hq} Hkv {Hkv} D {D} {dtype}, heads dealt to workgroups"
+    print(f"[decode] {what}", flush=True)
+    check(f64(out), ref_of(inp), what, ref_abs=ref_of(inp, True))
