@@ -447,15 +447,16 @@ def decode_partition_sweep(torch, dev):
     """Every row of the decode Shapes table, plus three shapes with few long
     contexts, timed with the library's own partition choice (partition_size
     0) and with forced 16- to 512-token partitions: per-launch time of 20
-    calls captured in a HIP graph and replayed 30 times.  One JSON line per
-    shape; `max_abs_diff` compares every forced split with the automatic
-    one."""
+    calls captured in a HIP graph, the median of 6 rounds of 10 replays (the
+    choices of a shape alternate in order from round to round).  One JSON
+    line per shape; `max_abs_diff` compares every forced split with the
+    automatic one."""
     sys.path.insert(0, os.path.join(ROOT, "tests", "golden"))
     import shapes
     from softmax_attention_flashattention_amd import attn_paged_decode, attn_paged_decode_num_partitions
     from softmax_attention_flashattention_amd import inputs as gen
 
-    def graph_us(call, per_graph=20, reps=30):
+    def capture(call, per_graph=20):
         for _ in range(3):
             call()
         torch.cuda.synchronize()
@@ -465,13 +466,23 @@ def decode_partition_sweep(torch, dev):
                 call()
         g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / (reps * per_graph) * 1e3
+        return g
+
+    def graph_us(graphs, per_graph=20, reps=10, rounds=6):
+        # rounds in alternating order, median per graph: no choice is timed
+        # only on a GPU that is still ramping up
+        ts = {k: [] for k in graphs}
+        keys = list(graphs)
+        for i in range(rounds):
+            for k in (keys if i % 2 == 0 else keys[::-1]):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(reps):
+                    graphs[k].replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts[k].append(a.elapsed_time(b) / (reps * per_graph) * 1e3)
+        return {k: round(sorted(v)[len(v) // 2], 2) for k, v in ts.items()}
 
     long_ctx = [dict(row="long-1", num_seqs=1, ctx_len=1024, num_query_heads=16, num_kv_heads=2,
                      head_size=128, dtype="bf16"),
@@ -484,20 +495,18 @@ def decode_partition_sweep(torch, dev):
                               r["head_size"], seed=3000, dtype=r["dtype"])
         d = {k: v.to(dev) for k, v in x.items()}
         maxb = x["block_tables"].shape[1]
-        times, diff, auto = {}, 0.0, None
+        graphs, outs = {}, {}
         for ps in (0, 16, 32, 64, 128, 256, 512):
             if ps >= 2 * max(r["ctx_len"], 16):
                 continue
-            out = torch.empty_like(d["query"])
-            call = lambda: attn_paged_decode(d["query"], d["k_cache"], d["v_cache"],
-                                             d["block_tables"], d["seq_lens"], out=out,
-                                             partition_size=ps)
-            times["auto" if ps == 0 else str(ps)] = round(graph_us(call), 2)
-            call()
-            torch.cuda.synchronize()
-            if auto is None:
-                auto = out.float().clone()
-            diff = max(diff, (out.float() - auto).abs().max().item())
+            key = "auto" if ps == 0 else str(ps)
+            out = outs[key] = torch.empty_like(d["query"])
+            graphs[key] = capture(lambda out=out, ps=ps: attn_paged_decode(
+                d["query"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"], out=out,
+                partition_size=ps))
+        times = graph_us(graphs)
+        auto = outs["auto"].float()
+        diff = max((o.float() - auto).abs().max().item() for o in outs.values())
         print(json.dumps({"decode_partitions": r["row"], "num_seqs": r["num_seqs"],
                           "ctx_len": r["ctx_len"], "num_query_heads": r["num_query_heads"],
                           "num_kv_heads": r["num_kv_heads"], "head_size": r["head_size"],
