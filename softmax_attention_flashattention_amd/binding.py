@@ -188,7 +188,9 @@ def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q=None, scal
         raise ValueError("out must have q's shape")
     if workspace is None:
         ws_len = _varlen_ws_bytes(num_seqs, max_seqlen_q, H, D, dev)
-        ws_ptr = torch.empty(ws_len, dtype=torch.uint8, device=q.device).data_ptr() if ws_len else None
+        # held until the call has enqueued its kernels
+        workspace = torch.empty(ws_len, dtype=torch.uint8, device=q.device) if ws_len else None
+        ws_ptr = workspace.data_ptr() if ws_len else None
     else:
         _need(workspace, "workspace", device=q.device)
         ws_len = workspace.numel() * workspace.element_size()
