@@ -40,9 +40,12 @@ def bar(gpu, ref, A, what):
 
 
 def run(x, scale=None):
+    # the output starts as NaN, so an element no workgroup writes fails the
+    # finiteness check
     d = to_gpu(x)
-    o = attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"], chunk_size=x.get("chunk_size", 64),
-                             scale=scale)
+    o = torch.full_like(d["v"], float("nan"))
+    attn_chunk_delta_out(d["q"], d["k"], d["v"], d["h"], d["g"], chunk_size=x.get("chunk_size", 64),
+                         scale=scale, out=o)
     torch.cuda.synchronize()
     return o
 
@@ -119,26 +122,12 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["chunk_t64_h32_hq16", "chunk_t704_h16_hq8", "chunk_t4195_h32_hq16"])
+@pytest.mark.parametrize("name", ["chunk_t64_h32_hq16", "chunk_t704_h16_hq8", "chunk_t4195_h32_hq16",
+                                  "chunk_t14807_h32_hq16"])
 def test_workloads_in_full(name):
+    # every element, the largest (14807 tokens x 32 heads, the benchmark's
+    # chunk workload) included
     full_check(gen.workload_inputs(name), name)
-
-
-def test_largest_workload_sampled_rows():
-    # the 14807-token, 32-head row of the Shapes table, as the benchmark runs
-    # it, checked on sampled (token, head) rows: the first and last tokens,
-    # chunk boundaries and random ones
-    name = "chunk_t14807_h32_hq16"
-    x = gen.workload_inputs(name)
-    print(f"[chunk] {name} sampled rows", flush=True)
-    out = f64(run(x))
-    T, H = 14807, 32
-    rng = np.random.default_rng(9)
-    toks = np.concatenate([[0, 1, 63, 64, 65, T - 24, T - 23, T - 1], rng.integers(0, T, 120)])
-    heads = rng.integers(0, H, toks.size)
-    ref = ch.chunk_delta_out_rows(x["q"], x["k"], x["v"], x["h"], x["g"], toks, heads)
-    A = ch.chunk_delta_out_rows(x["q"], x["k"], x["v"], x["h"], x["g"], toks, heads, absolute=True)
-    bar(out[0, toks, heads], ref, A, name)
 
 
 def test_binding_rejects_mismatched_tensors():
