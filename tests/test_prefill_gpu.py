@@ -4,9 +4,9 @@ Operator: atrex-bench "attention_forward" (#001), Reference Implementation.
 Every case feeds the HIP library and the oracle the same seeded inputs and
 applies the bar of tests/parity.py elementwise.  The full-size workloads run
 with their output filled with NaN first, so an unwritten row cannot pass:
-the 276- and 8136-token ones are compared on every element, the 16742- and
-65556-token ones on one row from every work item (plus one whole head of the
-16742-token one), after checking that every element was written.
+the 276-, 8136- and 16742-token ones are compared on every element, the
+65556-token one on one row from every work item after checking that every
+element was written.
 """
 import numpy as np
 import pytest
