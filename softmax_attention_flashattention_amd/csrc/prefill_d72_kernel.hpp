@@ -30,12 +30,16 @@
 // between 16-lane rows by v_permlane16_swap (see pv).
 //
 // Schedule of a step (K(t+1) and V(t) in LDS): the 10 S MFMAs of tile t+1
-// with the DMA of K(t+2) and V(t+1) among them; then the 12 PV MFMAs of tile
-// t with the row max of S(t+1) and its exponentials (P(t+1), computed with
-// the current running max) riding along.  The running max is raised only
-// when a row's new max passes it by more than 2^8; when a cheap per-lane test
-// says that may have happened (rarely after the first tile), a branch of
-// plain VALU work rescales O and redoes P(t+1) with the raised max.
+// with the DMA of K(t+2) and V(t+1) among them; the 12 PV MFMAs of tile t;
+// then the softmax of S(t+1) as one block of VALU work: its row max, a
+// raised running max where a cheap per-lane test says some row may have
+// passed it by more than 2^8 (rarely after the first tile; O is rescaled
+// then), and the exponentials, written over P(t) once the MFMAs have read
+// it.  The two waves of a SIMD come from different workgroups, so one's
+// VALU block runs beside the other's MFMAs: this order measured 0.8% faster
+// than the exponentials spread under the PV MFMAs, and 4-5% faster than
+// those pinned there (the head_dim-128 kernel, with more MFMAs per score,
+// measured the other way round).
 //
 // Softmax runs in the base-2 domain with c = |scale| log2(e); a negative
 // scale negates Q as it is loaded.  Keys past the end of the sequence get
@@ -267,7 +271,8 @@ void prefill_fwd_d72_kernel(PrefillParams p)
     // Raise the running max where some row passed it by more than the
     // threshold, rescaling O.  mx: this lane's max of raw scores of the new
     // tile per query block.  Called for the first tile and when the cheap
-    // per-lane test fired somewhere in the wave.
+    // per-lane test fired somewhere in the wave, before that tile's
+    // exponentials.
     auto rescale = [&](const float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -382,17 +387,15 @@ void prefill_fwd_d72_kernel(PrefillParams p)
         __syncthreads();   // K buffer 0 is refilled during the first step
     }
 
-    // ---- one step: S(t+1) (if has_next), then PV(t) with the softmax of
-    // S(t+1) riding along.  K(t) and V(t) live in buffer par, K(t+1) in npar;
-    // this step's DMA brings K(t+2) into par and V(t+1) into npar.  The four
-    // tile buffers come in restrict-qualified: the buffer parity is a run-time
-    // value, and without this the compiler cannot tell the tiles being read
-    // from those the DMA is filling and waits for the DMA before the first
-    // V^T read of every step.  Wave priority by phase: PV phase 2, S phase 1,
-    // rest 0 (the two waves of a SIMD come from different workgroups).  The
-    // PV phase carries all of the step's exponentials; letting it issue
-    // first measured 1.6-1.9% faster than the S phase first (the order the
-    // head_dim-128 kernel keeps, where it measured 1.3% better).
+    // ---- one step: S(t+1) (if has_next), PV(t), then the softmax of
+    // S(t+1).  K(t) and V(t) live in buffer par, K(t+1) in npar; this step's
+    // DMA brings K(t+2) into par and V(t+1) into npar.  The four tile buffers
+    // come in restrict-qualified: the buffer parity is a run-time value, and
+    // without this the compiler cannot tell the tiles being read from those
+    // the DMA is filling and waits for the DMA before the first V^T read of
+    // every step.  Wave priority by phase: PV 2, S 1, the softmax block 0
+    // (the two waves of a SIMD come from different workgroups, so the MFMAs
+    // of one issue ahead of the other's VALU work).
     auto step_bufs = [&](int t, const uint16_t *__restrict__ k_read, uint16_t *__restrict__ k_fill,
                          const uint16_t *__restrict__ v_read, uint16_t *__restrict__ v_fill, auto has_next,
                          auto masked) __attribute__((always_inline)) {
@@ -414,47 +417,17 @@ void prefill_fwd_d72_kernel(PrefillParams p)
             pv(vt, pw, [](int) {});
             setprio(std::integral_constant<int, 0>{});
         } else {
-            // PV(t) with the softmax of S(t+1) riding along: the row max of a
-            // query block under each of the first two slots, the 16
-            // exponential pairs spread over all six, into pn (the words of
-            // P(t) stay in use until the last slot).
-            float mx[2];
-            uint32_t pn[2][8];
-            bool raise = false;
-            pv(vt, pw, [&](int j) __attribute__((always_inline)) {
-                switch (j) {
-                case 0:
-                    lane_max1(s, mx, 0);
-                    exp_pair(s, pn, 0, t + 1, masked);
-                    exp_pair(s, pn, 8, t + 1, masked);
-                    break;
-                case 1:
-                    lane_max1(s, mx, 1);
-                    raise = needs_rescale(mx);   // wave-uniform; rare after the first tile
-                    exp_pair(s, pn, 1, t + 1, masked);
-                    exp_pair(s, pn, 9, t + 1, masked);
-                    break;
-                default:   // j = 2..5: three of the pairs 2-7 and 10-15, alternating blocks
-#pragma unroll
-                    for (int i = 0; i < 3; ++i) {
-                        const int k = 3 * (j - 2) + i;
-                        exp_pair(s, pn, (k & 1) ? 10 + (k >> 1) : 2 + (k >> 1), t + 1, masked);
-                    }
-                    break;
-                }
-            });
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pw[qb][i] = pn[qb][i];
+            // PV(t), then the softmax of S(t+1): its row max, a raised max
+            // where some row passed the threshold, and the exponentials,
+            // written over P(t) now that the MFMAs have read it
+            pv(vt, pw, [](int) {});
             setprio(std::integral_constant<int, 0>{});
-            if (raise) {
-                // some row's max rose past the threshold: rescale O and redo
-                // P(t+1) with the raised max
-                rescale(mx);
+            float mx[2];
+            lane_max1(s, mx, 0);
+            lane_max1(s, mx, 1);
+            if (needs_rescale(mx)) rescale(mx);   // wave-uniform; rare after the first tile
 #pragma unroll
-                for (int pi = 0; pi < 16; ++pi) exp_pair(s, pw, pi, t + 1, masked);
-            }
+            for (int pi = 0; pi < 16; ++pi) exp_pair(s, pw, pi, t + 1, masked);
         }
     };
 
