@@ -1,0 +1,87 @@
+"""Offsets past 2^31 elements (4 GiB of 16-bit data) in prefill and decode,
+against the oracle ("attention_forward" #001 and "paged_attention_decode"
+#024, Reference Implementation).
+
+The tensors repeat a seeded pattern (1000 token rows, or 1000 cache blocks)
+copied on the GPU, so that the inputs are cheap to build and the oracle only
+needs the pattern.  The period does not divide 2^31 elements, so a device
+offset that wrapped at 32 bits would read rows holding other values and fail
+the comparison.  The checked rows are those whose byte offsets lie past 2^32
+(and a few below, for contrast).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check, f64
+from softmax_attention_flashattention_amd import attn_paged_decode, attn_varlen_fwd, inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+PERIOD = 1000
+
+
+def tiled(x, n):
+    """x [PERIOD, ...] (CPU) repeated along dim 0 to n rows, on the GPU."""
+    reps = (n + x.shape[0] - 1) // x.shape[0]
+    return x.cuda().repeat(reps, *([1] * (x.dim() - 1)))[:n].contiguous()
+
+
+def test_prefill_offsets_past_4_gib():
+    # 17 x 2^20 tokens x 1 head x 128 dims: q, k, v and out are 4.56 GB each
+    # (element offsets up to 2.28e9); 17408 sequences of 1024 tokens
+    H, D, L = 1, 128, 1024
+    N = 17 << 20
+    nseq = N // L
+    pat = gen.prefill_inputs([PERIOD], H, D, seed=81)
+    print(f"[prefill] {N} tokens x {H} x {D}: offsets past 2^31 elements", flush=True)
+    q, k, v = tiled(pat["q"], N), tiled(pat["k"], N), tiled(pat["v"], N)
+    cu = torch.arange(0, N + 1, L, dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    attn_varlen_fwd(q, k, v, cu, cu, max_seqlen_q=L, out=out)
+    torch.cuda.synchronize()
+    first_high = (1 << 31) // (H * D) // L            # the first sequence past 2^31 elements
+    for s in [0, 5, first_high - 1, first_high, first_high + 1, nseq - 2, nseq - 1]:
+        rows = np.arange(s * L, (s + 1) * L) % PERIOD
+        idx = torch.from_numpy(rows)
+        qs, ks, vs = pat["q"][idx].contiguous(), pat["k"][idx].contiguous(), pat["v"][idx].contiguous()
+        cu1 = torch.tensor([0, L], dtype=torch.int32)
+        ref, ref_abs = oracle.varlen_fwd(qs, ks, vs, cu1, cu1, return_abs=True)
+        got = f64(out[s * L:(s + 1) * L])
+        check(got, ref, f"sequence {s} (element offsets from {s * L * H * D})", ref_abs=ref_abs)
+    del q, k, v, out, cu
+    torch.cuda.empty_cache()
+
+
+def test_decode_offsets_past_4_gib():
+    # 2^20 + 2^17 cache blocks of one KV head at head_size 128 (2048 elements
+    # a block): K and V caches are 4.8 GB each; the tables point at blocks on
+    # both sides of 2^20 (element offset 2^31)
+    Hq, Hkv, D, bs = 8, 1, 128, 16
+    nb = (1 << 20) + (1 << 17)
+    S, ctx = 8, 300
+    pat = gen.decode_inputs(1, PERIOD * bs, Hq, Hkv, D, seed=83, spare_blocks=0)
+    kp, vp = pat["k_cache"][:PERIOD], pat["v_cache"][:PERIOD]     # PERIOD distinct blocks
+    print(f"[decode] {nb} cache blocks: offsets past 2^31 elements", flush=True)
+    kc, vc = tiled(kp, nb), tiled(vp, nb)
+    rng = np.random.default_rng(85)
+    maxb = (ctx + bs - 1) // bs
+    bt = np.empty((S, maxb), dtype=np.int32)
+    for s in range(S):
+        lo = 0 if s < 2 else (1 << 20) - 8
+        bt[s] = rng.integers(lo, nb, maxb) if s >= 2 else rng.integers(0, 1 << 17, maxb)
+    bt[3] = np.arange(nb - maxb, nb)                    # the very last blocks
+    lens = np.array([ctx - 7 * s for s in range(S)], dtype=np.int32)
+    query = gen.decode_inputs(S, 1, Hq, Hkv, D, seed=87)["query"]
+    out = torch.full((S, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    attn_paged_decode(query.cuda(), kc, vc, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                      out=out)
+    torch.cuda.synchronize()
+    # the oracle on a small cache of the pattern blocks the tables name
+    small_bt = torch.from_numpy((bt % PERIOD).astype(np.int32))
+    ref = oracle.paged_decode(query, kp, vp, small_bt, torch.from_numpy(lens))
+    ref_abs = oracle.paged_decode(query, kp, vp.abs(), small_bt, torch.from_numpy(lens))
+    check(f64(out), ref, "decode, blocks past element offset 2^31", ref_abs=ref_abs)
+    del kc, vc, out
+    torch.cuda.empty_cache()
