@@ -1,10 +1,11 @@
-"""Offsets past 2^31 elements (4 GiB of 16-bit data) in prefill and decode,
-against the oracle ("attention_forward" #001 and "paged_attention_decode"
-#024, Reference Implementation).
+"""Offsets past 2^31 elements (4 GiB of 16-bit data) in prefill, decode and
+the chunked output, against the oracle ("attention_forward" #001,
+"paged_attention_decode" #024 and "chunk_delta_rule_output" #004, Reference
+Implementation).
 
-The tensors repeat a seeded pattern (1000 token rows, or 1000 cache blocks)
-copied on the GPU, so that the inputs are cheap to build and the oracle only
-needs the pattern.  The period does not divide 2^31 elements, so a device
+The tensors repeat a seeded pattern (1000 token rows, 1000 cache blocks or
+250 chunks) copied on the GPU, so that the inputs are cheap to build and the
+oracle only needs the pattern.  The period does not divide 2^31 elements, so a device
 offset that wrapped at 32 bits would read rows holding other values and fail
 the comparison.  The checked rows are those whose byte offsets lie past 2^32
 (and a few below, for contrast).
@@ -84,4 +85,38 @@ def test_decode_offsets_past_4_gib():
     ref_abs = oracle.paged_decode(query, kp, vp.abs(), small_bt, torch.from_numpy(lens))
     check(f64(out), ref, "decode, blocks past element offset 2^31", ref_abs=ref_abs)
     del kc, vc, out
+    torch.cuda.empty_cache()
+
+
+def test_chunk_output_offsets_past_4_gib():
+    # 9600 chunks of 64 tokens, 32 value / 16 query heads, key and value dim
+    # 128: h is 10 GB (element offsets up to 5.0e9), v and out 5 GB each.
+    # Each chunk's output depends on that chunk's q, k, v, g and state only,
+    # so the oracle checks a chunk on its pattern chunk alone.
+    import oracle.chunk as ch
+    from softmax_attention_flashattention_amd import attn_chunk_delta_out
+    from test_chunk_gpu import bar
+    Hq, H, cs, P = 16, 32, 64, 250                     # P pattern chunks
+    nc = 9600
+    T = nc * cs
+    pat = gen.chunk_inputs(1, P * cs, Hq, H, seed=89)
+    print(f"[chunk] {T} tokens x {H} heads: offsets past 2^31 elements", flush=True)
+
+    def tile_tokens(x):                                # [1, P*cs, ...] -> [1, T, ...]
+        return tiled(x[0], T).unsqueeze(0)
+    q, k, v, g = (tile_tokens(pat[n]) for n in ("q", "k", "v", "g"))
+    h = tiled(pat["h"][0], nc).unsqueeze(0)
+    out = torch.full_like(v, float("nan"))
+    attn_chunk_delta_out(q, k, v, h, g, chunk_size=cs, out=out)
+    torch.cuda.synchronize()
+    # h passes element offset 2^31 at chunk 4096, v and out at chunk 8192
+    for c in [0, 7, 4095, 4096, 4097, 8191, 8192, nc - 1]:
+        pc = c % P
+        t0 = pc * cs
+        one = {n: pat[n][:, t0:t0 + cs].contiguous() for n in ("q", "k", "v", "g")}
+        hc = pat["h"][:, pc:pc + 1].contiguous()
+        ref = ch.chunk_delta_out(one["q"], one["k"], one["v"], hc, one["g"])
+        A = ch.chunk_delta_out(one["q"], one["k"], one["v"], hc, one["g"], absolute=True)
+        bar(f64(out[:, c * cs:(c + 1) * cs]), ref, A, f"chunk {c}")
+    del q, k, v, g, h, out
     torch.cuda.empty_cache()
