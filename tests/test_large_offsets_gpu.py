@@ -120,3 +120,38 @@ def test_chunk_output_offsets_past_4_gib():
         bar(f64(out[:, c * cs:(c + 1) * cs]), ref, A, f"chunk {c}")
     del q, k, v, g, h, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("lens,H,D,path", [
+    ([300, 17, 290], 4, 72, "key-splitting workgroups"),
+    ([9000], 1, 72, "64-row waves, items split into key ranges"),
+    ([2116, 1500], 16, 72, "32-row waves"),
+    ([1000, 600], 2, 128, "head_dim 128, items split into key ranges"),
+])
+def test_prefill_segments_past_4_gib(lens, H, D, path):
+    # few work items whose segments start past element offset 2^31 of
+    # buffers of 4.3-4.6 GB: query and key segments begin at different rows,
+    # so every kernel path the grid selects addresses q, k, v and out far out
+    rs = H * D
+    a_q = (1 << 31) // rs + 123                  # first query row of the segments
+    a_k = (1 << 31) // rs + 777                  # first key row
+    tot = sum(lens)
+    nq, nk = a_q + tot, a_k + tot
+    pat = gen.prefill_inputs([PERIOD], H, D, seed=91 + D + H)
+    print(f"[prefill] {path}: segments {lens} x {H} heads at rows {a_q} (q), {a_k} (k, v)", flush=True)
+    q, k, v = tiled(pat["q"], nq), tiled(pat["k"], nk), tiled(pat["v"], nk)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lens)]) + a_q, dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lens)]) + a_k, dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    attn_varlen_fwd(q, k, v, cu_q, cu_k, max_seqlen_q=max(lens), out=out)
+    torch.cuda.synchronize()
+    qi = torch.from_numpy((np.arange(a_q, nq) % PERIOD))
+    ki = torch.from_numpy((np.arange(a_k, nk) % PERIOD))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    ref, ref_abs = oracle.varlen_fwd(pat["q"][qi].contiguous(), pat["k"][ki].contiguous(),
+                                     pat["v"][ki].contiguous(), cu, cu, return_abs=True)
+    check(f64(out[a_q:nq]), ref, f"{path}: segments past 2^31 elements", ref_abs=ref_abs)
+    # the rows before the segments are outside every segment: untouched
+    assert bool(torch.isnan(out[a_q - 64:a_q]).all()), f"{path}: rows before the segments written"
+    del q, k, v, out
+    torch.cuda.empty_cache()
