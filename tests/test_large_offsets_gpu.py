@@ -155,3 +155,36 @@ def test_prefill_segments_past_4_gib(lens, H, D, path):
     assert bool(torch.isnan(out[a_q - 64:a_q]).all()), f"{path}: rows before the segments written"
     del q, k, v, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("D", [72, 128])
+def test_prefill_largest_head_count(D):
+    # the most heads the library accepts, num_heads * head_dim < 2^25: one
+    # token row is then almost 64 MiB, so a 64-key tile spans almost 2^32
+    # bytes, the most its 32-bit byte offsets reach.  64 tokens, heads
+    # repeating a pattern of 1000 heads; the output is NaN-filled first and
+    # every element must be written; all heads of the first and last 3000
+    # and every 97th head are compared with the oracle
+    H = ((1 << 32) - 1) // (2 * 64 * D)          # largest H with H * D * 2 * 64 < 2^32
+    assert H * D * 2 * 64 < (1 << 32) <= (H + 1) * D * 2 * 64
+    S, HP = 64, 1000
+    pat = gen.prefill_inputs([S], HP, D, seed=93 + D)
+    print(f"[prefill] {S} tokens x {H} heads x {D}: key tiles spanning almost 2^32 bytes", flush=True)
+
+    def tile_heads(x):                             # [S, HP, D] -> [S, H, D] on the GPU
+        return x.cuda().repeat(1, (H + HP - 1) // HP, 1)[:, :H].contiguous()
+    q, k, v = tile_heads(pat["q"]), tile_heads(pat["k"]), tile_heads(pat["v"])
+    cu = torch.tensor([0, S], dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    attn_varlen_fwd(q, k, v, cu, cu, max_seqlen_q=S, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), f"D={D}: rows left unwritten or non-finite"
+    ref, ref_abs = oracle.varlen_fwd(pat["q"], pat["k"], pat["v"], pat["cu_seqlens_q"],
+                                     pat["cu_seqlens_k"], return_abs=True)
+    heads = np.unique(np.concatenate([np.arange(3000), np.arange(H - 3000, H), np.arange(0, H, 97)]))
+    for i in range(0, heads.size, 4096):
+        hs = heads[i:i + 4096]
+        got = f64(out[:, torch.from_numpy(hs).cuda()])
+        check(got, ref[:, hs % HP], f"D={D}, heads {hs[0]}..{hs[-1]}", ref_abs=ref_abs[:, hs % HP])
+    del q, k, v, out
+    torch.cuda.empty_cache()
