@@ -9,6 +9,7 @@
 #include "attn.h"
 #include "chunk_kernel.hpp"
 #include "decode_kernel.hpp"
+#include "decode_mfma_kernel.hpp"
 #include "prefill_d128_kernel.hpp"
 #include "prefill_d72_kernel.hpp"
 #include "prefill_kernel.hpp"
@@ -265,9 +266,24 @@ int launch_decode(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
     return launch_status();
 }
 
+// Grouped query heads held by one workgroup: the products on MFMAs
+template <typename T, int D>
+int launch_decode_mfma(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((attn::decode_mfma_kernel<T, D>), dim3(static_cast<unsigned>(grid)),
+                       dim3(attn::kDecodeThreads), 0, stream, p);
+    int rc = launch_status();
+    if (rc != ATTN_OK || p.num_parts == 1) return rc;
+    hipLaunchKernelGGL((attn::decode_merge_kernel<T, D>),
+                       dim3(static_cast<unsigned>(static_cast<int64_t>(p.num_seqs) * p.Hq)), dim3(64), 0,
+                       stream, p);
+    return launch_status();
+}
+
 template <typename T, int D>
 int dispatch_decode_g(const attn::DecodeParams &p, int64_t grid, hipStream_t stream)
 {
+    if (p.on_mfma) return launch_decode_mfma<T, D>(p, grid, stream);
     if (p.gsub <= 1) return launch_decode<T, D, 1>(p, grid, stream);
     if (p.gsub <= 2) return launch_decode<T, D, 2>(p, grid, stream);
     if (p.gsub <= 4) return launch_decode<T, D, 4>(p, grid, stream);
@@ -529,6 +545,20 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     const int gsub = (G + ngroups - 1) / ngroups;
     ngroups = (G + gsub - 1) / gsub;
     const int64_t grid = units * ngroups;
+    // One workgroup per KV head holding several query heads: the score and
+    // value products on MFMAs (decode_mfma_kernel) where that measured
+    // faster than VALU dot products, by query heads per KV head and the
+    // blocks a workgroup walks (graph-replayed, device-filling grids: at
+    // head_size 128, 16 query heads per KV head 1.8x at 64 tokens and 2.1x
+    // at 2048, 8 heads +9% at 64 tokens, 2 heads +11-14% from 256 tokens;
+    // with 1-4 heads and 128 tokens or fewer the VALU kernel wins by 7-68%,
+    // the MFMA kernel's merge over 16 padded heads then weighing on short
+    // workgroups.  At head_size 256, where the MFMA kernel runs one wave per
+    // SIMD: 16 heads 2.3-3x, 8 heads +15% at 512 tokens but -11% at 128,
+    // 1-4 heads level or slower.)
+    const int walk_blocks = part_blocks < max_blocks_per_seq ? part_blocks : max_blocks_per_seq;
+    const bool on_mfma = ngroups == 1 && (head_size == 128 ? (G >= 8 || (G >= 2 && walk_blocks >= 16))
+                                                              : (G >= 16 || (G >= 8 && walk_blocks >= 32)));
 
     attn::DecodeParams p;
     p.query = static_cast<const uint16_t *>(query);
@@ -559,6 +589,7 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     p.num_parts = np;
     p.gsub = gsub;
     p.ngroups = ngroups;
+    p.on_mfma = on_mfma ? 1 : 0;
     p.scale_log2e = scale * attn::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return dtype == ATTN_DTYPE_BF16 ? dispatch_decode<attn::Bf16>(p, head_size, grid, s)

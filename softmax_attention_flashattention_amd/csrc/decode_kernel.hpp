@@ -64,6 +64,7 @@ struct DecodeParams {
     int num_parts;
     int gsub;         // query heads per workgroup (G when the heads are not dealt out)
     int ngroups;      // workgroups per (sequence, KV head, partition): ceil(G / gsub)
+    int on_mfma;      // 1: decode_mfma_kernel (host-side choice, unused by the kernels)
     float scale_log2e;
 };
 

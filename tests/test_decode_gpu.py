@@ -225,3 +225,34 @@ def test_query_heads_dealt_to_workgroups(S, L, Hq, Hkv, D, dtype):
     what = f"decode {S} x {L} Hq {Hq} Hkv {Hkv} D {D} {dtype}, heads dealt to workgroups"
     print(f"[decode] {what}", flush=True)
     check(f64(out), ref_of(inp), what, ref_abs=ref_of(inp, True))
+
+
+@pytest.mark.parametrize("S,L,Hq,Hkv,D,dtype,ps", [
+    (64, 300, 32, 8, 128, "bf16", 0),       # G 4, 19 blocks a workgroup
+    (40, 700, 40, 8, 128, "fp16", 0),       # G 5: heads padded to 16 columns
+    (128, 300, 16, 8, 128, "fp16", 0),      # G 2 with 19 blocks
+    (70, 1000, 64, 4, 128, "bf16", 256),    # G 16, split context, merge kernel
+    (64, 400, 64, 8, 128, "bf16", 32),      # G 8, 2-block partitions: a block per wave
+    (48, 600, 64, 8, 256, "bf16", 0),       # G 8, head_size 256, 32 blocks a workgroup
+    (32, 900, 128, 8, 256, "fp16", 128),    # G 16, head_size 256, split context
+    (300, 17, 32, 4, 128, "bf16", 0),       # G 8, contexts of one or two blocks
+])
+def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
+    # device-filling grids (sequence x KV head x partition units at least the
+    # compute units) with grouped query heads run the score and value
+    # products on MFMAs (decode_mfma_kernel: at head_size 128 from 8 heads
+    # per KV head, or 2 with 16 blocks a workgroup; at 256 from 16, or 8 with
+    # 32 blocks); ragged contexts, an empty one, scattered blocks
+    lens = [L - (13 * i) % max(L // 2, 1) for i in range(S)]
+    lens[1] = 0
+    inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + Hq + D + ps, dtype=dtype, seq_lens=lens)
+    inp = gen.permute_blocks(inp, seed=S * 7 + Hq)
+    d = to_gpu(inp)
+    out = torch.full_like(d["query"], float("nan"))
+    attn_paged_decode(d["query"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"], out=out,
+                      partition_size=ps)
+    torch.cuda.synchronize()
+    what = f"decode {S} x {L} Hq {Hq} Hkv {Hkv} D {D} {dtype} partition {ps or 'auto'}, grouped heads on MFMAs"
+    print(f"[decode] {what}", flush=True)
+    check(f64(out), ref_of(inp), what, ref_abs=ref_of(inp, True))
+    assert torch.count_nonzero(out[1]).item() == 0, what
