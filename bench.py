@@ -48,10 +48,12 @@ KERNEL_SOURCES = {
     "prefill_fwd_kernel": ["prefill_kernel.hpp", "device_common.hpp"],
     "prefill_fwd_split_kernel": ["prefill_split_kernel.hpp", "prefill_kernel.hpp", "device_common.hpp"],
     "decode_partition_kernel": ["decode_kernel.hpp", "device_common.hpp"],
+    "decode_mfma_kernel": ["decode_mfma_kernel.hpp", "decode_kernel.hpp", "device_common.hpp"],
     "chunk_delta_out_kernel": ["chunk_kernel.hpp", "device_common.hpp"],
 }
 ALL_SOURCES = ["prefill_d128_kernel.hpp", "prefill_d72_kernel.hpp", "prefill_kernel.hpp",
-               "prefill_split_kernel.hpp", "decode_kernel.hpp", "chunk_kernel.hpp", "device_common.hpp"]
+               "prefill_split_kernel.hpp", "decode_kernel.hpp", "decode_mfma_kernel.hpp", "chunk_kernel.hpp",
+               "device_common.hpp"]
 # the page rows ("attention_forward" Shapes table) of the prefill workloads
 WORKLOAD_PAGE_ROWS = {"prefill_s276_h4_d72": 11, "prefill_s8136_h16_d72": 4,
                       "prefill_s16742_h32_d128": 9, "prefill_s65556_h16_d72": 8}
@@ -517,6 +519,58 @@ def decode_partition_sweep(torch, dev):
         del x, d
 
 
+# device-filling decode shapes with grouped query heads (sequences, context,
+# query heads, KV heads, head_size): where the library runs the score and
+# value products on MFMAs, and the one-query-head-per-KV-head cases beside
+GROUPED_DECODE_SHAPES = [
+    (64, 2048, 8, 8, 128), (64, 2048, 16, 8, 128), (64, 2048, 32, 8, 128), (64, 2048, 64, 8, 128),
+    (64, 2048, 128, 8, 128), (256, 512, 32, 8, 128), (256, 128, 64, 8, 128), (256, 64, 128, 8, 128),
+    (128, 1024, 16, 16, 256), (128, 512, 64, 8, 256), (32, 2048, 64, 4, 256), (64, 256, 128, 8, 256),
+]
+
+
+def decode_grouped(torch, dev):
+    """Paged decode on device-filling grids with 1-16 query heads per KV head:
+    per-launch time of 20 calls captured in a HIP graph (median of 6 rounds of
+    5 replays), the K/V bytes read per second, and which kernel the library
+    chose.  One JSON line per shape."""
+    from softmax_attention_flashattention_amd import attn_paged_decode
+    from softmax_attention_flashattention_amd import inputs as gen
+    for (S, ctx, hq, hkv, d) in GROUPED_DECODE_SHAPES:
+        x = gen.decode_inputs(S, ctx, hq, hkv, d, seed=4242)
+        t = {k: v.to(dev) for k, v in x.items()}
+        out = torch.empty_like(t["query"])
+        call = lambda: attn_paged_decode(t["query"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                         t["seq_lens"], out=out)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(20):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 100 * 1e3)
+        us = sorted(ts)[len(ts) // 2]
+        kv = 2 * S * ctx * hkv * d * 2
+        G = hq // hkv
+        print(json.dumps({"decode_grouped": f"{S}x{ctx}", "num_seqs": S, "ctx_len": ctx, "num_query_heads": hq,
+                          "num_kv_heads": hkv, "head_size": d, "query_heads_per_kv_head": G,
+                          "graph_us_per_launch": round(us, 2), "kv_bytes": kv,
+                          "gbs": round(kv / us / 1e3, 1), "frac": round(kv / us / 1e3 / PEAK_HBM_GBS, 4)}),
+              flush=True)
+        del x, t, out, g
+
+
 def page_context(p_host):
     """The pages' own times for the timed workloads (Shapes tables stored under
     tests/golden): T_SOL on hardware the pages label only "XPU-A", T_Prod on
@@ -566,6 +620,9 @@ def main():
     ap.add_argument("--decode-partitions", action="store_true",
                     help="time the decode Shapes rows and three few-long-context shapes with the "
                          "automatic and with forced context partitions (one JSON line each) and exit")
+    ap.add_argument("--decode-grouped", action="store_true",
+                    help="time device-filling decode shapes with 1-16 query heads per KV head "
+                         "(one JSON line each) and exit")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit "
                          "(no GPU needed)")
@@ -591,6 +648,8 @@ def main():
         return shapes_rows(torch, dev, args.shapes)
     if args.decode_partitions:
         return decode_partition_sweep(torch, dev)
+    if args.decode_grouped:
+        return decode_grouped(torch, dev)
 
     p_name = args.prefill_workload
     p_host = gen.workload_inputs(p_name)
