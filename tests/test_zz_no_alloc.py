@@ -72,3 +72,15 @@ def test_automatic_partitions_use_the_buffer():
     inp = gen.decode_inputs(2, 3000, 8, 1, 128, seed=203, seq_lens=[3000, 77])
     assert binding.attn_paged_decode_num_partitions(2, 1, inp["block_tables"].shape[1], 16) == 24
     compare(inp, 0, "2 seqs x 1 KV head x ctx <= 3000, automatic partitions")
+
+
+def test_grouped_heads_on_matrix_cores_use_the_buffer():
+    # 8 and 16 query heads per KV head on device-filling grids run on the
+    # MFMA decode kernel; their split contexts' partials go to the static
+    # buffer too (two calls, the second smaller)
+    big = gen.decode_inputs(64, 1000, 32, 4, 128, seed=204,
+                            seq_lens=[1000, 17, 0, 640, 999, 1, 512, 513] * 8)
+    compare(big, 256, "64 seqs x 32/4 heads x ctx <= 1000, partitions of 256 tokens, MFMA kernel")
+    small = gen.decode_inputs(32, 600, 64, 4, 256, seed=205, dtype="fp16",
+                              seq_lens=[600, 33, 1, 0, 288, 100, 17, 256] * 4)
+    compare(small, 128, "32 seqs x 64/4 heads x ctx <= 600, head_size 256, fp16, MFMA kernel")
