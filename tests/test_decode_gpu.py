@@ -241,8 +241,8 @@ def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
     # device-filling grids (sequence x KV head x partition units at least the
     # compute units) with grouped query heads run the score and value
     # products on MFMAs (decode_mfma_kernel: at head_size 128 from 8 heads
-    # per KV head, or 2 with 16 blocks a workgroup; at 256 from 16, or 8 with
-    # 32 blocks); ragged contexts, an empty one, scattered blocks
+    # per KV head, 4 with 8 blocks a workgroup or 2 with 16; at 256 from 16,
+    # or 8 with 32 blocks); ragged contexts, an empty one, scattered blocks
     lens = [L - (13 * i) % max(L // 2, 1) for i in range(S)]
     lens[1] = 0
     inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + Hq + D + ps, dtype=dtype, seq_lens=lens)
@@ -256,3 +256,31 @@ def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
     print(f"[decode] {what}", flush=True)
     check(f64(out), ref_of(inp), what, ref_abs=ref_of(inp, True))
     assert torch.count_nonzero(out[1]).item() == 0, what
+
+
+@pytest.mark.parametrize("S,L,Hq,Hkv,D,dtype,ps", [
+    (64, 300, 64, 8, 128, "bf16", 0),       # G 8, whole contexts
+    (64, 200, 128, 8, 256, "fp16", 0),      # G 16, head_size 256
+    (64, 700, 32, 8, 128, "bf16", 128),     # G 4, 8-block partitions, merge kernel
+])
+def test_identical_value_rows_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
+    # The invariant of test_identical_value_rows_return_that_row on grids
+    # that run the MFMA decode kernel: its row sum adds the same 16-bit
+    # weights that form the B operand of the value product, so every output
+    # row is the KV head's value row bit for bit, through the split-context
+    # merge too.
+    lens = [(1, 15, 16, 17, 100, L, L - 3, 33)[i % 8] for i in range(S)]
+    lens[5] = 0
+    inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=90 + S + Hq + D, dtype=dtype, seq_lens=lens)
+    inp["query"] = (inp["query"].float() * 4).to(inp["query"].dtype)
+    u = inp["v_cache"][0, :, :, 0].clone()                              # [Hkv, D]
+    inp["v_cache"] = u[None, :, :, None].expand_as(inp["v_cache"]).contiguous()
+    inp = gen.permute_blocks(inp, seed=S + D)
+    print(f"[decode] identical V rows on MFMAs {S} x {L} Hq {Hq} Hkv {Hkv} D {D} {dtype} partition {ps}",
+          flush=True)
+    out = run(inp, ps).cpu()
+    G = Hq // Hkv
+    for s, n in enumerate(lens):
+        for hq in range(Hq):
+            want = u[hq // G] if n > 0 else torch.zeros_like(u[0])
+            assert torch.equal(out[s, hq], want), (s, n, hq)
