@@ -552,13 +552,13 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     // head_size 128, 16 query heads per KV head 1.8x at 64 tokens and 2.1x
     // at 2048, 8 heads +9% at 64 tokens, 4 heads +7% at 128 tokens, 2 heads
     // +11-14% from 256 tokens; with 2-4 heads over 64-100 tokens the VALU
-    // kernel wins by 6-27%.  At head_size 256, where the MFMA kernel runs one
-    // wave per SIMD: 16 heads 2.3-3x, 8 heads +15% at 512 tokens but -11% at
-    // 128, 1-4 heads level or slower.)
+    // kernel wins by 5-27%.  At head_size 256: 16 heads 2.3-3x, 8 heads
+    // +3% at 64 tokens and +15-17% at 128-256, 4 heads +4-7% from 32 blocks a
+    // workgroup; with fewer blocks, and with 1-2 heads, level or slower.)
     const int walk_blocks = part_blocks < max_blocks_per_seq ? part_blocks : max_blocks_per_seq;
     const bool on_mfma =
         ngroups == 1 && (head_size == 128 ? (G >= 8 || (G >= 4 && walk_blocks >= 8) || (G >= 2 && walk_blocks >= 16))
-                                          : (G >= 16 || (G >= 8 && walk_blocks >= 32)));
+                                          : (G >= 8 || (G >= 4 && walk_blocks >= 32)));
 
     attn::DecodeParams p;
     p.query = static_cast<const uint16_t *>(query);

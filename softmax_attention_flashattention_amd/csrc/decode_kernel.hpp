@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
     constexpr int CHUNK = D * BS;       // elements of one (block, kv head) chunk
     __shared__ __attribute__((aligned(16))) uint32_t q_lds[GMAX][D / 2];   // 16-bit pairs
     __shared__ __attribute__((aligned(16))) float p_lds[NW][GMAX][BS];
-    __shared__ float m_lds[NW][GMAX], l_lds[NW][GMAX];
+    __shared__ float m_lds[NW][GMAX], l_lds[NW][GMAX], c_lds[NW][GMAX];
     __shared__ __attribute__((aligned(16))) float o_lds[NW][GMAX][D];
 
     const int tid = threadIdx.x;
@@ -237,31 +237,40 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += kDecodeThreads) {
-        const int g = i / D, d = i % D;
+    // per head, once: the waves' weights 2^(m_w - M) (zero for a wave that saw
+    // no token), folded with 1 / sum when this partition is the whole context
+    if (tid < G) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][g]);
-        float num = 0.f, den = 0.f;
-        if (M != -INFINITY) {
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][tid]);
+        float sw[NW], den = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = m_lds[w][g];
-                const float sc = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-                den += sc * l_lds[w][g];
-                num += sc * o_lds[w][g][d];
-            }
+        for (int w = 0; w < NW; ++w) {
+            const float mw = m_lds[w][tid];
+            sw[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            den += sw[w] * l_lds[w][tid];
         }
+        const float f = p.num_parts == 1 ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) c_lds[w][tid] = sw[w] * f;
+        if (p.num_parts > 1) {
+            const int64_t slot = (static_cast<int64_t>(s) * p.Hq + hq0 + tid) * p.num_parts + part;
+            p.ws_ml[slot * 2 + 0] = M;
+            p.ws_ml[slot * 2 + 1] = den;
+        }
+    }
+    __syncthreads();
+    // four dims of one head per thread: the weighted sum of the waves' O
+    for (int i = tid; i < G * (D / 4); i += kDecodeThreads) {
+        const int g = i / (D / 4), d = 4 * (i % (D / 4));
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) o += c_lds[w][g] * *reinterpret_cast<const f32x4 *>(&o_lds[w][g][d]);
         const int64_t row = static_cast<int64_t>(s) * p.Hq + hq0 + g;
         if (p.num_parts == 1) {
-            p.out[row * D + d] = T::from_f32(den > 0.f ? num / den : 0.f);
+            *reinterpret_cast<uint2 *>(p.out + row * D + d) = uint2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
         } else {
-            const int64_t slot = row * p.num_parts + part;
-            p.ws_o[slot * D + d] = num;
-            if (d == 0) {
-                p.ws_ml[slot * 2 + 0] = M;
-                p.ws_ml[slot * 2 + 1] = den;
-            }
+            *reinterpret_cast<f32x4 *>(p.ws_o + (row * p.num_parts + part) * D + d) = o;
         }
     }
 }

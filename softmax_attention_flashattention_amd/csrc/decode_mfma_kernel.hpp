@@ -30,9 +30,10 @@
 // online softmax per head (base-2 domain, running max
 // raised only when a score passes it by more than 2^8: the result is
 // shift-invariant); the row sum adds up the 16-bit weights that multiply V.
-// The four waves merge through LDS; a split context writes (max, sum,
-// unnormalised output) for decode_merge_kernel, as decode_partition_kernel
-// does.
+// The four waves merge through LDS (per head once: the waves' weights and the
+// reciprocal of the row sum; then four dims a thread); a split context writes
+// (max, sum, unnormalised output) for decode_merge_kernel, as
+// decode_partition_kernel does.
 #pragma once
 
 #include "decode_kernel.hpp"
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
     constexpr int KS = D / 32;          // 32-dim k-steps of a block's score product
     constexpr int DT = D / 16;          // 16-dim tiles of O^T
     constexpr int CHUNK = D * BS;       // elements of one (block, kv head) chunk
-    __shared__ float m_lds[NW][16], l_lds[NW][16];
+    __shared__ float m_lds[NW][16], l_lds[NW][16], c_lds[NW][16];
     __shared__ __attribute__((aligned(16))) float o_lds[NW][16][D];
 
     const int tid = threadIdx.x;
@@ -210,31 +211,40 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParam
             *reinterpret_cast<f32x4 *>(&o_lds[wave][g][16 * dt + 4 * q]) = oacc[dt];
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += kDecodeThreads) {
-        const int gi = i / D, d = i % D;
+    // per head, once: the waves' weights 2^(m_w - M) (zero for a wave that saw
+    // no token), folded with 1 / sum when this partition is the whole context
+    if (tid < G) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][gi]);
-        float num = 0.f, den = 0.f;
-        if (M != -INFINITY) {
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][tid]);
+        float sw[NW], den = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = m_lds[w][gi];
-                const float sw = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
-                den += sw * l_lds[w][gi];
-                num += sw * o_lds[w][gi][d];
-            }
+        for (int w = 0; w < NW; ++w) {
+            const float mw = m_lds[w][tid];
+            sw[w] = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            den += sw[w] * l_lds[w][tid];
         }
+        const float f = p.num_parts == 1 ? (den > 0.f ? 1.f / den : 0.f) : 1.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) c_lds[w][tid] = sw[w] * f;
+        if (p.num_parts > 1) {
+            const int64_t slot = (static_cast<int64_t>(s) * p.Hq + hq0 + tid) * p.num_parts + part;
+            p.ws_ml[slot * 2 + 0] = M;
+            p.ws_ml[slot * 2 + 1] = den;
+        }
+    }
+    __syncthreads();
+    // four dims of one head per thread: the weighted sum of the waves' O
+    for (int i = tid; i < G * (D / 4); i += kDecodeThreads) {
+        const int gi = i / (D / 4), d = 4 * (i % (D / 4));
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += c_lds[w][gi] * *reinterpret_cast<const f32x4 *>(&o_lds[w][gi][d]);
         const int64_t row = static_cast<int64_t>(s) * p.Hq + hq0 + gi;
         if (p.num_parts == 1) {
-            p.out[row * D + d] = T::from_f32(den > 0.f ? num / den : 0.f);
+            *reinterpret_cast<uint2 *>(p.out + row * D + d) = uint2{pack2<T>(acc[0], acc[1]), pack2<T>(acc[2], acc[3])};
         } else {
-            const int64_t slot = row * p.num_parts + part;
-            p.ws_o[slot * D + d] = num;
-            if (d == 0) {
-                p.ws_ml[slot * 2 + 0] = M;
-                p.ws_ml[slot * 2 + 1] = den;
-            }
+            *reinterpret_cast<f32x4 *>(p.ws_o + (row * p.num_parts + part) * D + d) = acc;
         }
     }
 }

@@ -236,13 +236,15 @@ def test_query_heads_dealt_to_workgroups(S, L, Hq, Hkv, D, dtype):
     (48, 600, 64, 8, 256, "bf16", 0),       # G 8, head_size 256, 32 blocks a workgroup
     (32, 900, 128, 8, 256, "fp16", 128),    # G 16, head_size 256, split context
     (300, 17, 32, 4, 128, "bf16", 0),       # G 8, contexts of one or two blocks
+    (128, 130, 64, 8, 256, "fp16", 0),      # G 8, head_size 256, 9 blocks a workgroup
+    (64, 600, 32, 8, 256, "bf16", 0),       # G 4, head_size 256, 38 blocks a workgroup
 ])
 def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
     # device-filling grids (sequence x KV head x partition units at least the
     # compute units) with grouped query heads run the score and value
     # products on MFMAs (decode_mfma_kernel: at head_size 128 from 8 heads
-    # per KV head, 4 with 8 blocks a workgroup or 2 with 16; at 256 from 16,
-    # or 8 with 32 blocks); ragged contexts, an empty one, scattered blocks
+    # per KV head, 4 with 8 blocks a workgroup or 2 with 16; at 256 from 8,
+    # or 4 with 32 blocks); ragged contexts, an empty one, scattered blocks
     lens = [L - (13 * i) % max(L // 2, 1) for i in range(S)]
     lens[1] = 0
     inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + Hq + D + ps, dtype=dtype, seq_lens=lens)
