@@ -545,20 +545,14 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     const int gsub = (G + ngroups - 1) / ngroups;
     ngroups = (G + gsub - 1) / gsub;
     const int64_t grid = units * ngroups;
-    // One workgroup per KV head holding several query heads: the score and
-    // value products on MFMAs (decode_mfma_kernel) where that measured
-    // faster than VALU dot products, by query heads per KV head and the
-    // blocks a workgroup walks (graph-replayed, device-filling grids: at
-    // head_size 128, 16 query heads per KV head 1.8x at 64 tokens and 2.1x
-    // at 2048, 8 heads +9% at 64 tokens, 4 heads +7% at 128 tokens, 2 heads
-    // +11-14% from 256 tokens; with 2-4 heads over 64-100 tokens the VALU
-    // kernel wins by 5-27%.  At head_size 256: 16 heads 2.3-3x, 8 heads
-    // +3% at 64 tokens and +15-17% at 128-256, 4 heads +4-7% from 32 blocks a
-    // workgroup; with fewer blocks, and with 1-2 heads, level or slower.)
-    const int walk_blocks = part_blocks < max_blocks_per_seq ? part_blocks : max_blocks_per_seq;
-    const bool on_mfma =
-        ngroups == 1 && (head_size == 128 ? (G >= 8 || (G >= 4 && walk_blocks >= 8) || (G >= 2 && walk_blocks >= 16))
-                                          : (G >= 8 || (G >= 4 && walk_blocks >= 32)));
+    // One workgroup per KV head holding two or more query heads (no head
+    // dealing): the score and value products on MFMAs (decode_mfma_kernel).
+    // Graph-replayed against the VALU dot-product kernel on device-filling
+    // grids, it ran faster or level at every shape measured: 16 query heads
+    // per KV head 1.8x at 64 tokens and 2.1x at 2048; 4 heads 12-16% over
+    // 48-100 tokens; 2 heads 2-10% over 16-200 tokens; at head_size 256, 2-4
+    // heads 6-17%, 16 heads 3x.
+    const bool on_mfma = ngroups == 1 && G >= 2;
 
     attn::DecodeParams p;
     p.query = static_cast<const uint16_t *>(query);

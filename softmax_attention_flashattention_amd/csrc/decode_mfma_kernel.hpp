@@ -57,7 +57,7 @@ __device__ __forceinline__ uint2 ld8_stream(const void *p) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeParams p)
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 2))) void decode_mfma_kernel(DecodeParams p)
 {
     constexpr int BS = kDecodeBS, NW = kDecodeWaves;
     constexpr int KS = D / 32;          // 32-dim k-steps of a block's score product

@@ -238,13 +238,16 @@ def test_query_heads_dealt_to_workgroups(S, L, Hq, Hkv, D, dtype):
     (300, 17, 32, 4, 128, "bf16", 0),       # G 8, contexts of one or two blocks
     (128, 130, 64, 8, 256, "fp16", 0),      # G 8, head_size 256, 9 blocks a workgroup
     (64, 600, 32, 8, 256, "bf16", 0),       # G 4, head_size 256, 38 blocks a workgroup
+    (512, 40, 16, 8, 128, "bf16", 0),       # G 2, three blocks a workgroup
+    (256, 50, 24, 8, 128, "fp16", 0),       # G 3 over four blocks
+    (256, 70, 16, 8, 256, "bf16", 0),       # G 2, head_size 256
 ])
 def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
     # device-filling grids (sequence x KV head x partition units at least the
     # compute units) with grouped query heads run the score and value
-    # products on MFMAs (decode_mfma_kernel: at head_size 128 from 8 heads
-    # per KV head, 4 with 8 blocks a workgroup or 2 with 16; at 256 from 8,
-    # or 4 with 32 blocks); ragged contexts, an empty one, scattered blocks
+    # products on MFMAs (decode_mfma_kernel, from 2 query heads per KV head
+    # when no heads are dealt out); ragged contexts, an empty one, scattered
+    # blocks
     lens = [L - (13 * i) % max(L // 2, 1) for i in range(S)]
     lens[1] = 0
     inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + Hq + D + ps, dtype=dtype, seq_lens=lens)
