@@ -551,8 +551,12 @@ int launch_paged_decode(const void *query, const void *k_cache, const void *v_ca
     // grids, it ran faster or level at every shape measured: 16 query heads
     // per KV head 1.8x at 64 tokens and 2.1x at 2048; 4 heads 12-16% over
     // 48-100 tokens; 2 heads 2-10% over 16-200 tokens; at head_size 256, 2-4
-    // heads 6-17%, 16 heads 3x.
-    const bool on_mfma = ngroups == 1 && G >= 2;
+    // heads 6-17%, 16 heads 3x.  With one query head per KV head only where a
+    // workgroup walks 8 blocks or more (3% at 128 tokens, 5% at head_size
+    // 256 over 1024; over 64 tokens the VALU kernel is 1-2% ahead, 12% at
+    // head_size 256).
+    const int walk_blocks = part_blocks < max_blocks_per_seq ? part_blocks : max_blocks_per_seq;
+    const bool on_mfma = ngroups == 1 && (G >= 2 || walk_blocks >= 8);
 
     attn::DecodeParams p;
     p.query = static_cast<const uint16_t *>(query);

@@ -241,13 +241,16 @@ def test_query_heads_dealt_to_workgroups(S, L, Hq, Hkv, D, dtype):
     (512, 40, 16, 8, 128, "bf16", 0),       # G 2, three blocks a workgroup
     (256, 50, 24, 8, 128, "fp16", 0),       # G 3 over four blocks
     (256, 70, 16, 8, 256, "bf16", 0),       # G 2, head_size 256
+    (256, 130, 16, 16, 128, "bf16", 0),     # one query head per KV head, 9 blocks a workgroup
+    (128, 300, 8, 8, 256, "fp16", 0),       # one query head per KV head, head_size 256
+    (64, 1000, 8, 8, 128, "bf16", 128),     # one query head per KV head, 8-block partitions, merge
 ])
 def test_grouped_heads_on_matrix_cores(S, L, Hq, Hkv, D, dtype, ps):
     # device-filling grids (sequence x KV head x partition units at least the
     # compute units) with grouped query heads run the score and value
     # products on MFMAs (decode_mfma_kernel, from 2 query heads per KV head
-    # when no heads are dealt out); ragged contexts, an empty one, scattered
-    # blocks
+    # when no heads are dealt out, with one where a workgroup walks 8 blocks
+    # or more); ragged contexts, an empty one, scattered blocks
     lens = [L - (13 * i) % max(L // 2, 1) for i in range(S)]
     lens[1] = 0
     inp = gen.decode_inputs(S, L, Hq, Hkv, D, seed=S + Hq + D + ps, dtype=dtype, seq_lens=lens)
